@@ -1,0 +1,31 @@
+"""CPU oracle for the paged-KV attention forward.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or run anything in this
+package.  The library (``invariant_paged_kv_amd``) never imports it, and it
+never imports the library: the two share no code.  Both are fed by the seeded
+generators in ``pkv_inputs``, which hold none of the method's arithmetic.
+
+The oracle is plain NumPy in float64.  It computes the mathematical definition
+of the operation, with no blocking, chunking, online softmax or fixed-order
+merging: those are how the GPU path reaches the same result, not what the
+result is.
+
+Pins (see ``tests/test_oracle.py``): every function here is checked against
+something other than itself -- a pure-Python ``decimal`` brute force over a
+nested-list pool, PyTorch's own float64 scaled-dot-product attention, closed
+forms, and the invariances the pages state.  No function in this package is
+"parity unpinned".
+"""
+
+from .paged_kv import (  # noqa: F401
+    Layout,
+    attention,
+    bf16_bits_to_f64,
+    cache_write,
+    gather_sequence,
+    masked_softmax,
+    scores,
+    row_positions,
+    visible_keys,
+)
