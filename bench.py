@@ -1,0 +1,220 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one generate step of the long-context decode workload: append one
+new token's K/V per sequence with pkv_cache_write, then attend that token
+against the whole paged context with pkv_attn_forward (split kernel + fixed
+order merge).  Workload: batch 16, Hq 64, Hkv 8, d 128, bf16, 131072 cached
+keys per sequence, block_size 256, K/V-interleaved cache (block stride
+2*256*8*128), random-permutation block table, N(0,1) values, causal.
+
+Prints one JSON line: value = KV bytes read per second (GB/s) over the timed
+steps, the roofline of the attention launch (bytes it must move / its HIP-event
+duration vs 8 TB/s HBM), the oracle's throughput on a bounded sample of the
+same work on the host's cores, a prefill figure (TFLOP/s of the full causal
+prefill of batch 8 x 8192 tokens, Hq 16, Hkv 4), and bitwise checks.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--seqlen-k", type=int, default=131072)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU sharding (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import invariant_paged_kv_amd as pkv
+    import pkv_inputs as gen
+
+    dev = "cuda"
+    B, HQ, HK, D, BS = args.batch, 64, 8, 128, 256
+    N = args.seqlen_k
+    nb = gen.pool_num_blocks(N, BS, B)
+    gdev = torch.Generator(device=dev).manual_seed(1005)
+    pool = gen.new_pool(nb, BS, HK, D, "bf16", "interleaved", device=dev, generator=gdev)
+    bt = gen.randperm_block_table(nb, B, generator=torch.Generator().manual_seed(1005)).to(dev)
+    q = gen.randn((B, HQ, D), "bf16", generator=gdev, device=dev)
+    kn = gen.randn((B, HK, D), "bf16", generator=gdev, device=dev)
+    vn = gen.randn((B, HK, D), "bf16", generator=gdev, device=dev)
+    pos = torch.full((B,), N - 1, dtype=torch.int32, device=dev)   # the new token's position
+    seqlens = pos + 1
+    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, HQ), dtype=torch.float32, device=dev)
+    ws_bytes = pkv.workspace_size(q, pool.k, pool.v, bt, max_seqlen_q=1, max_seqlen_k=N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pkv.cache_write(kn, vn, pool.k, pool.v, bt, pos, cu)
+        ev0.record(stream)
+        pkv.attn_forward(q, pool.k, pool.v, bt, seqlens, cu, True, scale, max_seqlen_q=1, max_seqlen_k=N,
+                         out=out, lse=lse, workspace=ws)
+        ev1.record(stream)
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    attn_ms = 0.0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+        ev1.synchronize()
+        attn_ms += ev0.elapsed_time(ev1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    attn_avg_ms = attn_ms / args.steps
+
+    kv_bytes = B * N * HK * D * 2 * 2
+    attn_bytes = kv_bytes + 2 * q.numel() * 2 + lse.numel() * 4 + B * math.ceil(N / BS) * 4 + 2 * (B + 1) * 4
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+
+    # bitwise: the prefill kernel on the same rows gives the same bits
+    with pkv.options(path=2):
+        p_out, p_lse = pkv.attn_forward(q, pool.k, pool.v, bt, seqlens, cu, True, scale, max_seqlen_q=1,
+                                        max_seqlen_k=N)
+    torch.cuda.synchronize()
+    bitwise = bool(torch.equal(p_out.view(torch.int16), out.view(torch.int16))
+                   and torch.equal(p_lse.view(torch.int32), lse.view(torch.int32)))
+
+    result = {
+        "metric": "decode KV GB/s (% HBM peak) + prefill TFLOP/s; decode==prefill bitwise",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1), seeded",
+        "config": {
+            "workload": "long-context decode step: append 1 token + attend over 131072 cached keys",
+            "batch": B, "num_heads_q": HQ, "num_heads_k": HK, "head_dim": D, "seqlen_k": N,
+            "block_size": BS, "layout": "kv_interleaved", "block_table": "randperm", "causal": True,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "pkv_attn_forward (split + merge)",
+            "avg_ms": round(attn_avg_ms, 4),
+            "bytes_per_launch": attn_bytes,
+        },
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "bitwise_decode_eq_prefill_kernel": bitwise,
+    }
+    del ws, p_out, p_lse
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(torch, pkv, gen)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale)
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(torch, pkv, gen, reps: int = 3):
+    """Full causal prefill, batch 8 x 8192 tokens, Hq 16, Hkv 4, d 128, bs 16 (TFLOP/s of causal pairs)."""
+    dev = "cuda"
+    B, HQ, HK, D, BS, S = 8, 16, 4, 128, 16, 8192
+    nb = gen.pool_num_blocks(S, BS, B)
+    g = torch.Generator(device=dev).manual_seed(1004)
+    pool = gen.new_pool(nb, BS, HK, D, "bf16", "contiguous", device=dev, generator=g)
+    bt = gen.randperm_block_table(nb, B, generator=torch.Generator().manual_seed(1004)).to(dev)
+    q = gen.randn((B * S, HQ, D), "bf16", generator=g, device=dev)
+    sk = torch.full((B,), S, dtype=torch.int32, device=dev)
+    cu = torch.arange(0, B * S + 1, S, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+
+    def call():
+        return pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu, True, scale, max_seqlen_q=S, max_seqlen_k=S)
+
+    call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 4.0 * D * HQ * B * (S * (S + 1) / 2)
+    tf = flops / (ms * 1e-3) / 1e12
+    del pool
+    torch.cuda.empty_cache()
+    return {"workload": "full causal prefill batch 8 x 8192, Hq 16, Hkv 4, d 128, bs 16",
+            "ms": round(ms, 3), "tflops": round(tf, 2), "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": flops}
+
+
+def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, budget_s: float = 12.0):
+    """The float64 oracle on whole sequences of the same decode step, timed on the host."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    nblk = math.ceil(N / BS)
+    done, spent, seqs = 0, 0.0, 0
+    B, HQ = q.shape[0], q.shape[1]
+    for b in range(B):
+        ids = bt[b, :nblk].long()
+        kh = pool.k.index_select(0, ids).cpu().contiguous()
+        vh = pool.v.index_select(0, ids).cpu().contiguous()
+        kf = kh.view(torch.int16).numpy().view(np.uint16).reshape(-1)
+        vf = vh.view(torch.int16).numpy().view(np.uint16).reshape(-1)
+        row = HK * D
+        lay = oracle.Layout("bf16", HQ, HK, D, BS, 0, (BS * row, row, D), 0, (BS * row, row, D))
+        qh = q[b:b + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.attention(qh, kf, vf, lay, np.arange(nblk, dtype=np.int32)[None, :], [N], [0, 1], True, scale)
+        spent += time.perf_counter() - t0
+        seqs += 1
+        done += N * HK * D * 2 * 2
+        if spent >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(done / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{seqs} of {B} sequences of one decode step (all {HQ} heads, {N} keys each), "
+                      f"{spent:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * pkv.h -- batch-invariant paged-KV attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Plain pointers and sizes; every device pointer is a HIP
+ * device address on the current device; every call is asynchronous on the
+ * given stream and never synchronises the host.  No exceptions or aborts cross
+ * this boundary: each entry point returns PKV_OK (0) or a negative PKV_ERR_*
+ * code, and pkv_last_error() gives the calling thread's last message.
+ *
+ * What is computed (the operation these entry points implement):
+ *
+ *   RL-Kernel issue #152 "[WS1] KV-cache path consistency (prefill & decode)",
+ *   section Scope: attention of a query against N cached keys/values (decode)
+ *   must reduce in the same fixed order as the equivalent prefill over the full
+ *   sequence, and cache writes/reads must add no precision difference.
+ *   RL-Kernel PR #284 "feat(attention): add CP backward drift validation",
+ *   section Changes: a fixed KV chunk size, partials merged in ascending global
+ *   block index, fp32 accumulation, one downcast at the final write, and an
+ *   attention-domain LSE reported with the output.
+ *
+ *   For sequence b with n = seqlens_k[b] keys and L = cu_seqlens_q[b+1] -
+ *   cu_seqlens_q[b] query rows, row r sits at key position p = n - L + r
+ *   (bottom-right alignment) and sees keys j < n, and with causal also j <= p.
+ *   Query head h reads KV head h / (Hq / Hkv).  For each (row, head):
+ *       s_j = softmax_scale * <q, k_j>,   lse = ln(sum_j exp(s_j)),
+ *       out = sum_j exp(s_j - lse) v_j.
+ *   A row that sees no key gets out = 0 and lse = -inf.
+ *
+ * Reduction contract (what makes the result independent of batch size,
+ * padding, split count, grid and decode/prefill path):
+ *   keys are cut into chunks of PKV_CHUNK_KEYS keys at global key positions
+ *   [c*PKV_CHUNK_KEYS, (c+1)*PKV_CHUNK_KEYS); inside a chunk, tiles of
+ *   PKV_TILE_KEYS keys are accumulated in ascending order with an fp32 running
+ *   max; each chunk yields (max, sum, o[d]) in fp32; the chunk results of a row
+ *   are folded in ascending chunk index; the output is rounded once, at the
+ *   final write.  Every row's bits are a function of that row's query, its
+ *   visible keys/values and softmax_scale only.
+ *
+ * Memory layout (ROCm/aiter commit d293d61bbf19 "test(triton/decode): pin
+ * non-contiguous paged KV block stride"): the cache is paged in blocks of
+ * block_size tokens; key j of sequence b is in block block_table[b][j /
+ * block_size] at slot j % block_size.  K and V are each addressed by element
+ * strides (block, slot, head) with the head-dim stride 1, so both the
+ * contiguous [num_blocks, block_size, Hkv, d] layout and the K/V-interleaved
+ * [num_blocks, 2, block_size, Hkv, d] layout (block stride 2*block_size*Hkv*d)
+ * are served from their real strides.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+#define PKV_CHUNK_KEYS 512  /* keys per chunk: the unit partials are merged in */
+#define PKV_TILE_KEYS 64    /* keys per tile inside a chunk */
+
+/* Element type of q, the cache, new K/V and out.  lse is always fp32. */
+enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 };
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,      /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,     /* inconsistent or unsupported sizes */
+  PKV_ERR_DTYPE = -3,     /* unsupported dtype */
+  PKV_ERR_ALIGN = -4,     /* a pointer or stride breaks 16-byte alignment */
+  PKV_ERR_WORKSPACE = -5, /* workspace too small or could not be allocated */
+  PKV_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_OPTION = -7     /* unknown option or value */
+};
+
+/*
+ * Shapes and strides of one call.  All strides are in elements.
+ *   dtype               pkv_dtype of q, k/v cache, new K/V and out
+ *   batch               B, number of sequences
+ *   num_heads_q         Hq; num_heads_q % num_heads_k == 0
+ *   num_heads_k         Hkv
+ *   head_dim            d, 64 or 128
+ *   block_size          tokens per cache block, >= 1
+ *   max_blocks_per_seq  row length of block_table ([batch, max_blocks_per_seq], int32)
+ *   max_seqlen_q        host-side bound on every cu_seqlens_q[b+1] - cu_seqlens_q[b]
+ *   max_seqlen_k        host-side bound on every seqlens_k[b]; 0 means
+ *                       max_blocks_per_seq * block_size
+ *   total_q             rows of q / out / lse (cu_seqlens_q[batch])
+ *   num_blocks          blocks in the pool (used only by debug checks)
+ *   k_* / v_*_stride    element strides of the K and V caches: block, slot, head
+ * q and out are packed [total_q, Hq, d]; lse is [total_q, Hq] fp32.
+ */
+typedef struct pkv_layout {
+  int32_t dtype;
+  int32_t batch;
+  int32_t num_heads_q;
+  int32_t num_heads_k;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t max_seqlen_q;
+  int64_t max_seqlen_k;
+  int64_t total_q;
+  int64_t num_blocks;
+  int64_t k_block_stride, k_slot_stride, k_head_stride;
+  int64_t v_block_stride, v_slot_stride, v_head_stride;
+} pkv_layout;
+
+/*
+ * Attention forward over the paged cache.
+ *   q            device, [total_q, Hq, d] of dtype; rows cu_seqlens_q[b]..cu_seqlens_q[b+1]-1
+ *                belong to sequence b; Q/K are attention-ready (post-RoPE, RL-Kernel PR #284,
+ *                section "RoPE / TE Boundary"): no positional transform is applied here
+ *   k_cache      device, K elements addressed by kv_strides->k_* strides
+ *   v_cache      device, V elements addressed by kv_strides->v_* strides
+ *   kv_strides   host, shapes and strides (read during the call only)
+ *   block_table  device int32 [batch, max_blocks_per_seq]; only the first
+ *                ceil(seqlens_k[b] / block_size) entries of row b are read
+ *   seqlens_k    device int32 [batch]: keys visible to the call, including the keys
+ *                of this call's own query rows
+ *   cu_seqlens_q device int32 [batch + 1], non-decreasing, cu_seqlens_q[0] = 0
+ *   causal       nonzero: row at position p sees keys <= p
+ *   softmax_scale  multiplies <q, k> (e.g. 1/sqrt(d))
+ *   out          device, [total_q, Hq, d] of dtype (written)
+ *   lse          device fp32 [total_q, Hq] (written): natural-log LSE
+ *   stream       HIP stream; all work is enqueued there
+ * Buffers must stay alive until the stream passes this call.  Device data
+ * preconditions (not checked): block ids in [0, num_blocks); seqlens_k[b] <=
+ * min(max_seqlen_k, max_blocks_per_seq * block_size); row counts <=
+ * max_seqlen_q; cache values at visible positions finite.  The split (decode)
+ * path needs a workspace; this entry point takes it from the stream-ordered
+ * allocator (hipMallocAsync / hipFreeAsync on `stream`).
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_ALIGN (q, caches,
+ * out must be 16-byte aligned and every stride a multiple of 16 bytes),
+ * PKV_ERR_WORKSPACE, PKV_ERR_HIP.  Nothing is launched on error.
+ */
+int pkv_attn_forward(const void* q, const void* k_cache, const void* v_cache,
+                     const pkv_layout* kv_strides, const int32_t* block_table,
+                     const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
+                     float softmax_scale, void* out, float* lse, hipStream_t stream);
+
+/*
+ * As pkv_attn_forward, with a caller-owned device workspace of
+ * workspace_bytes >= pkv_attn_workspace_size(kv_strides) bytes (16-byte
+ * aligned).  Calls sharing one workspace must be ordered on one stream.
+ */
+int pkv_attn_forward_ws(const void* q, const void* k_cache, const void* v_cache,
+                        const pkv_layout* kv_strides, const int32_t* block_table,
+                        const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
+                        float softmax_scale, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes the split path needs for this layout (0 if it is never used). */
+size_t pkv_attn_workspace_size(const pkv_layout* kv_strides);
+
+/*
+ * Append new K/V rows to the paged cache.  RL-Kernel issue #152, section Scope:
+ * the write is a bit copy, so the path that wrote the cache and the path that
+ * reads it see the same values.
+ *   k_new, v_new    device, [total_new, Hkv, d] of dtype, packed
+ *   k_cache/v_cache device, addressed by kv_strides (written)
+ *   block_table     device int32 [batch, max_blocks_per_seq]
+ *   seqlens_k       device int32 [batch]: tokens already in the cache; token t of
+ *                   sequence b goes to position seqlens_k[b] + t.  Not updated: the
+ *                   caller advances it.
+ *   cu_seqlens_new  device int32 [batch + 1]
+ *   total_new       host copy of cu_seqlens_new[batch]
+ * Only the written slots change.  Precondition (not checked): every target
+ * position is < max_blocks_per_seq * block_size and maps to a valid block.
+ */
+int pkv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const pkv_layout* kv_strides, const int32_t* block_table,
+                    const int32_t* seqlens_k, const int32_t* cu_seqlens_new,
+                    int64_t total_new, hipStream_t stream);
+
+/* Host-only check of a layout (no device call).  Returns PKV_OK or an error. */
+int pkv_validate_layout(const pkv_layout* kv_strides);
+
+/*
+ * Process-wide tuning and test hooks.  None changes a result bit: they choose
+ * which kernels run and how work is split.
+ *   PKV_OPT_PATH          0 auto, 1 split (decode kernels + merge), 2 full (prefill kernel)
+ *   PKV_OPT_SPLIT_CHUNKS  chunks handled by one split work item (0 = auto, 1..64)
+ */
+enum pkv_option { PKV_OPT_PATH = 1, PKV_OPT_SPLIT_CHUNKS = 2 };
+int pkv_set_option(int option, int64_t value);
+int64_t pkv_get_option(int option);
+
+const char* pkv_error_string(int code);
+/* Message of the calling thread's last failed call ("" if none). */
+const char* pkv_last_error(void);
+int pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

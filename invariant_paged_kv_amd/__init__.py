@@ -1,0 +1,267 @@
+"""Python binding of libpkv, the batch-invariant paged-KV attention library.
+
+Argument marshalling only: shapes and strides are read from torch tensors,
+pointers and the current HIP stream are passed to the C ABI of ``libpkv.so``
+(``include/pkv.h``), and every step of the computation runs in its HIP kernels.
+PyTorch provides device memory and streams.  There is no fallback: if the
+library is not built, every call raises.
+
+    out, lse = attn_forward(q, k_cache, v_cache, block_table, seqlens_k,
+                            cu_seqlens_q, causal=True, softmax_scale=d**-0.5,
+                            max_seqlen_q=...)
+    cache_write(k_new, v_new, k_cache, v_cache, block_table, seqlens_k,
+                cu_seqlens_new, total_new)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_F32, PKV_BF16 = 0, 1
+PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS = 1, 2
+CHUNK_KEYS = 512
+TILE_KEYS = 64
+
+# Every symbol include/pkv.h declares.
+EXPORTS = (
+    "pkv_attn_forward",
+    "pkv_attn_forward_ws",
+    "pkv_attn_workspace_size",
+    "pkv_cache_write",
+    "pkv_validate_layout",
+    "pkv_set_option",
+    "pkv_get_option",
+    "pkv_error_string",
+    "pkv_last_error",
+    "pkv_abi_version",
+)
+
+
+class PkvLayout(ctypes.Structure):
+    """Mirror of ``pkv_layout`` in include/pkv.h."""
+
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("num_heads_q", ctypes.c_int32),
+        ("num_heads_k", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int64),
+        ("total_q", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int64),
+        ("k_block_stride", ctypes.c_int64),
+        ("k_slot_stride", ctypes.c_int64),
+        ("k_head_stride", ctypes.c_int64),
+        ("v_block_stride", ctypes.c_int64),
+        ("v_slot_stride", ctypes.c_int64),
+        ("v_head_stride", ctypes.c_int64),
+    ]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where}: {msg} (code {code})")
+        self.code = code
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libpkv.so``; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m invariant_paged_kv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lay = ctypes.POINTER(PkvLayout)
+    L.pkv_attn_forward.argtypes = [vp, vp, vp, lay, vp, vp, vp, i32, f32, vp, vp, vp]
+    L.pkv_attn_forward.restype = i32
+    L.pkv_attn_forward_ws.argtypes = [vp, vp, vp, lay, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.pkv_attn_forward_ws.restype = i32
+    L.pkv_attn_workspace_size.argtypes = [lay]
+    L.pkv_attn_workspace_size.restype = sz
+    L.pkv_cache_write.argtypes = [vp, vp, vp, vp, lay, vp, vp, vp, i64, vp]
+    L.pkv_cache_write.restype = i32
+    L.pkv_validate_layout.argtypes = [lay]
+    L.pkv_validate_layout.restype = i32
+    L.pkv_set_option.argtypes = [i32, i64]
+    L.pkv_set_option.restype = i32
+    L.pkv_get_option.argtypes = [i32]
+    L.pkv_get_option.restype = i64
+    L.pkv_error_string.argtypes = [i32]
+    L.pkv_error_string.restype = ctypes.c_char_p
+    L.pkv_last_error.argtypes = []
+    L.pkv_last_error.restype = ctypes.c_char_p
+    L.pkv_abi_version.argtypes = []
+    L.pkv_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        L = lib()
+        raise PkvError(rc, where, (L.pkv_last_error() or L.pkv_error_string(rc)).decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return PKV_BF16
+    if t == torch.float32:
+        return PKV_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def make_layout(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                num_heads_q: int, max_seqlen_q: int, total_q: int, max_seqlen_k: int = 0,
+                batch: Optional[int] = None) -> PkvLayout:
+    """``pkv_layout`` from the cache views' shapes and strides.
+
+    ``k_cache``/``v_cache`` are ``[num_blocks, block_size, Hkv, d]`` views with
+    unit stride in the last dimension; any block/slot/head strides (e.g. the
+    K/V-interleaved layout) are passed through as they are.
+    """
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_blocks, block_size, Hkv, d] with equal shapes")
+    if k_cache.stride(3) != 1 or v_cache.stride(3) != 1:
+        raise ValueError("the head-dim stride of k_cache and v_cache must be 1")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache dtypes differ")
+    nb, bs, hk, d = k_cache.shape
+    L = PkvLayout()
+    L.dtype = _dtype_code(k_cache.dtype)
+    L.batch = block_table.shape[0] if batch is None else batch
+    L.num_heads_q = num_heads_q
+    L.num_heads_k = hk
+    L.head_dim = d
+    L.block_size = bs
+    L.max_blocks_per_seq = block_table.shape[1]
+    L.max_seqlen_q = max_seqlen_q
+    L.max_seqlen_k = max_seqlen_k
+    L.total_q = total_q
+    L.num_blocks = nb
+    L.k_block_stride, L.k_slot_stride, L.k_head_stride = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    L.v_block_stride, L.v_slot_stride, L.v_head_stride = v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)
+    return L
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _int32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_table: torch.Tensor, seqlens_k: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                 causal: bool, softmax_scale: float, *, max_seqlen_q: int, max_seqlen_k: int = 0,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention of packed queries ``q [total_q, Hq, d]`` against the paged cache.
+
+    ``seqlens_k[b]`` keys are visible to sequence ``b`` (including its own new
+    rows); rows ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]`` are its queries, row
+    ``r`` at key position ``seqlens_k[b] - L + r``.  ``max_seqlen_q`` (and
+    optionally ``max_seqlen_k``) are host-side bounds.  Returns ``(out, lse)``:
+    ``out`` like ``q``, ``lse [total_q, Hq]`` fp32 natural-log LSE.
+    """
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [total_q, Hq, d] tensor")
+    if q.dtype != k_cache.dtype:
+        raise TypeError("q and cache dtypes differ")
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k)
+    if lay.head_dim != q.shape[2]:
+        raise ValueError("q head_dim differs from the cache's")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    bt = _int32(block_table, "block_table")
+    sk = _int32(seqlens_k, "seqlens_k")
+    cu = _int32(cu_seqlens_q, "cu_seqlens_q")
+    L = lib()
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(lay), bt.data_ptr(),
+            sk.data_ptr(), cu.data_ptr(), 1 if causal else 0, float(softmax_scale), out.data_ptr(),
+            lse.data_ptr())
+    if workspace is None:
+        rc = L.pkv_attn_forward(*args, _stream_handle(q.device))
+    else:
+        rc = L.pkv_attn_forward_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream_handle(q.device))
+    _check(rc, "pkv_attn_forward")
+    return out, lse
+
+
+def workspace_size(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                   *, max_seqlen_q: int, max_seqlen_k: int = 0) -> int:
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k)
+    return int(lib().pkv_attn_workspace_size(ctypes.byref(lay)))
+
+
+def cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_table: torch.Tensor, seqlens_k: torch.Tensor, cu_seqlens_new: torch.Tensor,
+                total_new: Optional[int] = None) -> None:
+    """Bit-copy ``k_new``/``v_new`` ``[total_new, Hkv, d]`` into the paged cache.
+
+    Token ``t`` of sequence ``b`` goes to key position ``seqlens_k[b] + t``;
+    ``seqlens_k`` is not advanced.
+    """
+    if total_new is None:
+        total_new = k_new.shape[0]
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if t.dim() != 3 or not t.is_contiguous() or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be a contiguous [total_new, Hkv, d] tensor of the cache dtype")
+    lay = make_layout(k_cache, v_cache, block_table, k_cache.shape[2], 0, 0)
+    L = lib()
+    rc = L.pkv_cache_write(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           ctypes.byref(lay), _int32(block_table, "block_table").data_ptr(),
+                           _int32(seqlens_k, "seqlens_k").data_ptr(),
+                           _int32(cu_seqlens_new, "cu_seqlens_new").data_ptr(), int(total_new),
+                           _stream_handle(k_new.device))
+    _check(rc, "pkv_cache_write")
+
+
+def set_option(option: int, value: int) -> None:
+    _check(lib().pkv_set_option(option, value), "pkv_set_option")
+
+
+def get_option(option: int) -> int:
+    return int(lib().pkv_get_option(option))
+
+
+class options:
+    """Context manager that sets library options and restores them on exit."""
+
+    def __init__(self, path: Optional[int] = None, split_chunks: Optional[int] = None):
+        self._want = {}
+        if path is not None:
+            self._want[PKV_OPT_PATH] = path
+        if split_chunks is not None:
+            self._want[PKV_OPT_SPLIT_CHUNKS] = split_chunks
+        self._old = {}
+
+    def __enter__(self):
+        for k, v in self._want.items():
+            self._old[k] = get_option(k)
+            set_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self._old.items():
+            set_option(k, v)
+        return False

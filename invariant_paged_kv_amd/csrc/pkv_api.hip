@@ -1,0 +1,297 @@
+// pkv_api.hip -- host side of libpkv: the C ABI declared in include/pkv.h.
+//
+// Validates every argument on the host before anything is launched, picks the
+// path (split + merge for few query columns per KV head, full/prefill kernel
+// otherwise), sizes the split path's fp32 partial buffers, and enqueues the
+// kernels on the caller's stream.  No host synchronisation, no exceptions
+// across the boundary: every entry point returns a pkv_status code and leaves
+// a message for pkv_last_error().
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kChunk = PKV_CHUNK_KEYS;
+static_assert(PKV_CHUNK_KEYS == 512 && PKV_TILE_KEYS == 64, "header constants must match the device code");
+
+thread_local char g_msg[512] = "";
+std::atomic<int64_t> g_opt_path{0};
+std::atomic<int64_t> g_opt_split_chunks{0};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_msg[0] = '\0';
+  return PKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+
+int64_t max_seqlen_k_of(const pkv_layout& l) {
+  const int64_t cap = static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size;
+  return (l.max_seqlen_k > 0 && l.max_seqlen_k < cap) ? l.max_seqlen_k : cap;
+}
+
+int validate(const pkv_layout* l) {
+  if (!l) return fail(PKV_ERR_NULL, "kv_strides (layout) is NULL");
+  if (l->dtype != PKV_F32 && l->dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "dtype %d is not PKV_F32 or PKV_BF16", l->dtype);
+  if (l->batch < 0) return fail(PKV_ERR_SHAPE, "batch %d < 0", l->batch);
+  if (l->num_heads_k < 1 || l->num_heads_q < 1 || l->num_heads_q % l->num_heads_k != 0)
+    return fail(PKV_ERR_SHAPE, "num_heads_q %d must be a positive multiple of num_heads_k %d", l->num_heads_q, l->num_heads_k);
+  if (l->head_dim != 64 && l->head_dim != 128) return fail(PKV_ERR_SHAPE, "head_dim %d is not 64 or 128", l->head_dim);
+  if (l->block_size < 1) return fail(PKV_ERR_SHAPE, "block_size %d < 1", l->block_size);
+  if (l->max_blocks_per_seq < 0) return fail(PKV_ERR_SHAPE, "max_blocks_per_seq %d < 0", l->max_blocks_per_seq);
+  if (static_cast<int64_t>(l->max_blocks_per_seq) * l->block_size > (int64_t{1} << 30))
+    return fail(PKV_ERR_SHAPE, "max_blocks_per_seq * block_size exceeds 2^30 keys");
+  if (l->max_seqlen_q < 0 || l->total_q < 0 || l->max_seqlen_k < 0 || l->num_blocks < 0)
+    return fail(PKV_ERR_SHAPE, "negative max_seqlen_q, max_seqlen_k, total_q or num_blocks");
+  if (static_cast<int64_t>(l->max_seqlen_q) * (l->num_heads_q / l->num_heads_k) > (int64_t{1} << 30))
+    return fail(PKV_ERR_SHAPE, "max_seqlen_q * (num_heads_q / num_heads_k) too large");
+  const int64_t s[6] = {l->k_block_stride, l->k_slot_stride, l->k_head_stride,
+                        l->v_block_stride, l->v_slot_stride, l->v_head_stride};
+  const int eb = elem_bytes(l->dtype);
+  for (int i = 0; i < 6; ++i) {
+    if (s[i] < 0) return fail(PKV_ERR_SHAPE, "negative cache stride");
+    if ((s[i] * eb) % 16 != 0) return fail(PKV_ERR_ALIGN, "cache stride %lld elements is not a multiple of 16 bytes", (long long)s[i]);
+  }
+  return ok();
+}
+
+struct Plan {
+  pkv::LaunchPlan lp;
+  int ncb;
+  int maxc;
+  int cpi;
+  size_t ws_bytes;
+  size_t off_ml;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
+
+Plan make_plan(const pkv_layout& l) {
+  Plan p{};
+  const int g = l.num_heads_q / l.num_heads_k;
+  const int64_t cols = static_cast<int64_t>(l.max_seqlen_q) * g;
+  const int64_t mk = max_seqlen_k_of(l);
+  p.maxc = static_cast<int>((mk + kChunk - 1) / kChunk);
+  const int64_t force = g_opt_path.load();
+  bool full;
+  int waves = 1;
+  if (force == 1) {
+    full = false;
+  } else if (force == 2) {
+    full = true;
+  } else if (cols <= 16) {
+    full = false;
+  } else {
+    const int64_t full_items = static_cast<int64_t>(l.batch) * l.num_heads_k * ((cols + 127) / 128);
+    full = full_items >= 512;
+  }
+  if (!full) waves = cols <= 16 ? 1 : 4;
+  const int cols_per_block = full ? 128 : 16 * waves;
+  p.ncb = static_cast<int>(std::max<int64_t>(1, (cols + cols_per_block - 1) / cols_per_block));
+  int64_t cpi = g_opt_split_chunks.load();
+  if (cpi <= 0) cpi = 1;
+  p.cpi = static_cast<int>(cpi);
+  p.lp.full = full;
+  p.lp.waves = waves;
+  p.lp.items = std::max(1, (p.maxc + p.cpi - 1) / p.cpi);
+  p.lp.batch = l.batch;
+  p.lp.hk = l.num_heads_k;
+  p.lp.total_q = l.total_q;
+  if (full || l.total_q == 0 || p.maxc == 0) {
+    p.ws_bytes = 0;
+  } else {
+    const size_t parts = static_cast<size_t>(l.total_q) * l.num_heads_q * p.maxc;
+    p.off_ml = round256(parts * l.head_dim * sizeof(float));
+    p.ws_bytes = p.off_ml + round256(parts * 2 * sizeof(float));
+  }
+  return p;
+}
+
+int check_attn_ptrs(const void* q, const void* k, const void* v, const int32_t* bt, const int32_t* sk,
+                    const int32_t* cu, const void* out, const float* lse, const pkv_layout& l) {
+  if (l.total_q > 0 && (!q || !out || !lse)) return fail(PKV_ERR_NULL, "q, out or lse is NULL");
+  if (l.batch > 0 && (!sk || !cu)) return fail(PKV_ERR_NULL, "seqlens_k or cu_seqlens_q is NULL");
+  if (l.batch > 0 && l.max_blocks_per_seq > 0 && (!k || !v || !bt)) return fail(PKV_ERR_NULL, "k_cache, v_cache or block_table is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(PKV_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+  return PKV_OK;
+}
+
+int run_attention(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* l,
+                  const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
+                  float softmax_scale, void* out, float* lse, void* ws, size_t ws_bytes, bool own_ws,
+                  hipStream_t stream) {
+  int rc = validate(l);
+  if (rc) return rc;
+  rc = check_attn_ptrs(q, k_cache, v_cache, block_table, seqlens_k, cu_seqlens_q, out, lse, *l);
+  if (rc) return rc;
+  if (!std::isfinite(softmax_scale)) return fail(PKV_ERR_SHAPE, "softmax_scale is not finite");
+  if (l->batch == 0 || l->total_q == 0) return ok();
+  const Plan p = make_plan(*l);
+  bool allocated = false;
+  if (p.ws_bytes > 0) {
+    if (own_ws) {
+      if (hipMallocAsync(&ws, p.ws_bytes, stream) != hipSuccess)
+        return fail(PKV_ERR_WORKSPACE, "hipMallocAsync of %zu workspace bytes failed", p.ws_bytes);
+      allocated = true;
+    } else if (!ws || ws_bytes < p.ws_bytes || !aligned16(ws)) {
+      return fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", p.ws_bytes, ws_bytes);
+    }
+  }
+  pkv::AttnArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.block_table = block_table;
+  a.seqlens_k = seqlens_k;
+  a.cu_q = cu_seqlens_q;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = p.ws_bytes ? static_cast<float*>(ws) : nullptr;
+  a.part_ml = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ml) : nullptr;
+  a.kbs = l->k_block_stride;
+  a.kss = l->k_slot_stride;
+  a.khs = l->k_head_stride;
+  a.vbs = l->v_block_stride;
+  a.vss = l->v_slot_stride;
+  a.vhs = l->v_head_stride;
+  a.hq = l->num_heads_q;
+  a.g = l->num_heads_q / l->num_heads_k;
+  a.bs = l->block_size;
+  a.mbps = l->max_blocks_per_seq;
+  a.ncb = p.ncb;
+  a.maxc = p.maxc;
+  a.cpi = p.cpi;
+  a.causal = causal ? 1 : 0;
+  a.mul = l->dtype == PKV_BF16 ? static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634074)
+                               : softmax_scale;
+  hipError_t e = pkv::launch_attention(a, p.lp, l->dtype, l->head_dim, stream);
+  if (allocated) {
+    hipError_t fe = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && fe != hipSuccess) e = fe;
+  }
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_validate_layout(const pkv_layout* kv_strides) { return validate(kv_strides); }
+
+size_t pkv_attn_workspace_size(const pkv_layout* kv_strides) {
+  if (validate(kv_strides) != PKV_OK) return 0;
+  return make_plan(*kv_strides).ws_bytes;
+}
+
+int pkv_attn_forward(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* kv_strides,
+                     const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
+                     float softmax_scale, void* out, float* lse, hipStream_t stream) {
+  return run_attention(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, causal, softmax_scale,
+                       out, lse, nullptr, 0, true, stream);
+}
+
+int pkv_attn_forward_ws(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* kv_strides,
+                        const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
+                        float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return run_attention(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, causal, softmax_scale,
+                       out, lse, workspace, workspace_bytes, false, stream);
+}
+
+int pkv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const pkv_layout* l,
+                    const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_new,
+                    int64_t total_new, hipStream_t stream) {
+  int rc = validate(l);
+  if (rc) return rc;
+  if (total_new < 0) return fail(PKV_ERR_SHAPE, "total_new %lld < 0", (long long)total_new);
+  if (total_new > 0x7fffffff) return fail(PKV_ERR_SHAPE, "total_new %lld exceeds 2^31-1", (long long)total_new);
+  if (total_new == 0 || l->batch == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seqlens_k || !cu_seqlens_new)
+    return fail(PKV_ERR_NULL, "a cache_write pointer is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_ALIGN, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
+  pkv::CacheWriteArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seqlens_k = seqlens_k;
+  a.cu_new = cu_seqlens_new;
+  a.kbs = l->k_block_stride;
+  a.kss = l->k_slot_stride;
+  a.khs = l->k_head_stride;
+  a.vbs = l->v_block_stride;
+  a.vss = l->v_slot_stride;
+  a.vhs = l->v_head_stride;
+  a.batch = l->batch;
+  a.hk = l->num_heads_k;
+  a.bs = l->block_size;
+  a.mbps = l->max_blocks_per_seq;
+  a.row_bytes = l->head_dim * elem_bytes(l->dtype);
+  hipError_t e = pkv::launch_cache_write(a, elem_bytes(l->dtype), total_new, stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "cache_write launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int pkv_set_option(int option, int64_t value) {
+  switch (option) {
+    case PKV_OPT_PATH:
+      if (value < 0 || value > 2) return fail(PKV_ERR_OPTION, "PKV_OPT_PATH must be 0, 1 or 2");
+      g_opt_path.store(value);
+      return ok();
+    case PKV_OPT_SPLIT_CHUNKS:
+      if (value < 0 || value > 64) return fail(PKV_ERR_OPTION, "PKV_OPT_SPLIT_CHUNKS must be in 0..64");
+      g_opt_split_chunks.store(value);
+      return ok();
+    default:
+      return fail(PKV_ERR_OPTION, "unknown option %d", option);
+  }
+}
+
+int64_t pkv_get_option(int option) {
+  switch (option) {
+    case PKV_OPT_PATH: return g_opt_path.load();
+    case PKV_OPT_SPLIT_CHUNKS: return g_opt_split_chunks.load();
+    default: return -1;
+  }
+}
+
+const char* pkv_error_string(int code) {
+  switch (code) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "null pointer";
+    case PKV_ERR_SHAPE: return "invalid or unsupported shape";
+    case PKV_ERR_DTYPE: return "unsupported dtype";
+    case PKV_ERR_ALIGN: return "misaligned pointer or stride";
+    case PKV_ERR_WORKSPACE: return "workspace too small or unavailable";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_OPTION: return "invalid option";
+    default: return "unknown error";
+  }
+}
+
+const char* pkv_last_error(void) { return g_msg; }
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// pkv_cache_write.hip -- append new K/V rows to the paged cache (bit copy).
+//
+// RL-Kernel issue #152 "[WS1] KV-cache path consistency (prefill & decode)",
+// section Scope: the cache write must not change the stored values, so the
+// path that wrote the cache and the path that reads it see the same bits.
+// Token t of sequence b lands at key position seqlens_k[b] + t: block
+// block_table[b][pos / block_size], slot pos % block_size, addressed with the
+// cache's real strides (aiter commit d293d61bbf19: contiguous or
+// K/V-interleaved blocks).
+#include "pkv_internal.h"
+
+namespace pkv {
+
+typedef uint32_t u32x4_cw __attribute__((ext_vector_type(4)));
+
+// One work group per new token; threads copy 16-byte pieces of the token's
+// K and V rows (all KV heads).
+__global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int eb) {
+  const int64_t tok = blockIdx.x;
+  int lo = 0, hi = a.batch;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_new[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  if (b >= a.batch) return;
+  const int64_t pos = a.seqlens_k[b] + (tok - a.cu_new[b]);
+  const int64_t blk = a.block_table[(int64_t)b * a.mbps + pos / a.bs];
+  const int64_t slot = pos % a.bs;
+  const int cpr = a.row_bytes / 16;
+  const int per_tensor = a.hk * cpr;
+  for (int i = threadIdx.x; i < 2 * per_tensor; i += blockDim.x) {
+    const int tensor = i / per_tensor;
+    const int rem = i - tensor * per_tensor;
+    const int h = rem / cpr;
+    const int part = rem - h * cpr;
+    const unsigned char* src = static_cast<const unsigned char*>(tensor ? a.v_new : a.k_new) +
+                               (tok * a.hk + h) * a.row_bytes + 16 * part;
+    const int64_t off = tensor ? (blk * a.vbs + slot * a.vss + h * a.vhs) : (blk * a.kbs + slot * a.kss + h * a.khs);
+    unsigned char* dst = static_cast<unsigned char*>(tensor ? a.v_cache : a.k_cache) + off * eb + 16 * part;
+    *reinterpret_cast<u32x4_cw*>(dst) = *reinterpret_cast<const u32x4_cw*>(src);
+  }
+}
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, int elem_bytes, int64_t total_new, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (total_new == 0) return hipSuccess;
+  hipLaunchKernelGGL(cache_write_kernel, dim3(static_cast<unsigned>(total_new)), dim3(256), 0, stream, a, elem_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

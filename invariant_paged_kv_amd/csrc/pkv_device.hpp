@@ -1,0 +1,312 @@
+// pkv_device.hpp -- device code shared by every attention kernel of libpkv (gfx950).
+//
+// Everything that decides a result bit lives here, in one copy, and every
+// kernel (split/decode, merge, full/prefill) calls it: the QK^T and PV MFMA
+// chains with their fixed k-slot assignment, the tile softmax with its fixed
+// summation order, the chunk fold and the final division/rounding.  Kernels
+// differ only in how data reaches these functions (which loads, which lanes,
+// which grid), never in the arithmetic.
+//
+// The reduction order is the one RL-Kernel PR #284 ("feat(attention): add CP
+// backward drift validation", section Changes) records for its deterministic
+// reference: a fixed KV chunk size, partials merged in ascending global block
+// index, fp32 accumulation, and a single downcast at the final write.  Keys
+// are cut into chunks at global positions, so the same key always lands in the
+// same chunk, tile and MFMA k-slot, whichever call, batch or grid computes it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int KT = 64;   // keys per tile (online-softmax step inside a chunk)
+constexpr int KC = 512;  // keys per chunk (unit of split partials and of the fold)
+static_assert(KC % KT == 0, "a chunk is a whole number of tiles");
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define PKV_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---------------------------------------------------------------------------
+// Element types.  TBf16: bf16 storage, MFMA 16x16x32 bf16 -> fp32, base-2
+// softmax (scores pre-multiplied by scale*log2(e), exp2 via v_exp_f32).
+// TF32: fp32 storage, MFMA 16x16x4 fp32, natural-base expf/logf (the fp32
+// tolerances leave no room for the base-2 rewrite's extra rounding).
+// ---------------------------------------------------------------------------
+struct TBf16 {
+  static constexpr int EB = 2;  // bytes per element
+  static constexpr bool kBase2 = true;
+};
+struct TF32 {
+  static constexpr int EB = 4;
+  static constexpr bool kBase2 = false;
+};
+
+template <class T> __device__ __forceinline__ float pkv_exp(float x);
+template <> __device__ __forceinline__ float pkv_exp<TBf16>(float x) { return __builtin_amdgcn_exp2f(x); }
+template <> __device__ __forceinline__ float pkv_exp<TF32>(float x) { return expf(x); }
+
+// Natural-log LSE from the running max m and sum l (m in the score units of T).
+template <class T> __device__ __forceinline__ float pkv_lse(float m, float l);
+template <> __device__ __forceinline__ float pkv_lse<TBf16>(float m, float l) {
+  return (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;  // v_log_f32 is log2
+}
+template <> __device__ __forceinline__ float pkv_lse<TF32>(float m, float l) { return m + logf(l); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).  Result in the low 16 bits.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles.  A tile holds KT consecutive keys (tile-local row = key - j0) of
+// one KV head, row-major with a 16-byte pad per row.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+struct TileGeom {
+  static constexpr int ROW_BYTES = D * T::EB;          // 256 for bf16 d=128
+  static constexpr int PITCH = ROW_BYTES + 16;         // bytes between rows in LDS
+  static constexpr int CPR = ROW_BYTES / 16;           // 16-byte chunks per row
+  static constexpr int BYTES = KT * PITCH;             // one tensor's tile
+  static constexpr int NK = ROW_BYTES / 64;            // 64-byte column groups (QK steps)
+  static constexpr int DT = D / 16;                    // PV output d-tiles
+  static constexpr int MT = KT / 16;                   // 16-key M tiles per tile
+};
+
+// ---------------------------------------------------------------------------
+// Per-wave state of one chunk (online softmax over its tiles), for NT groups
+// of 16 query columns.  Lane l serves column 16*nt + l%16 and, in the O^T
+// accumulators, head-dim rows 16*dt + 4*(l/16) + i.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+struct ChunkState {
+  f32x4 o[NT][D / 16];
+  float m[NT];  // running max of the chunk (score units)
+  float l[NT];  // this lane's partial row sum (lanes of a column are summed at chunk end)
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void chunk_reset(ChunkState<D, NT>& st) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    st.m[nt] = -INFINITY;
+    st.l[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st.o[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Q operands of one column group: lane l holds bytes [64k + 16*(l/16), +16) of
+// its column's query row, k = 0 .. NK-1.  (bf16: the 8 elements that fill MFMA
+// k-slots 8G..8G+7 of QK step k; fp32: 4 elements feeding 4 MFMA steps.)
+template <class T, int D>
+struct QOps {
+  u32x4 v[TileGeom<T, D>::NK];
+};
+
+// ---------------------------------------------------------------------------
+// QK^T for one tile: S^T[key][col] = sum over d of K[key][d] * Q[col][d].
+// K (A operand) comes from the LDS tile; Q (B operand) from registers.
+// bf16 k-slot map of step k: slot 8G+e <-> d = 32k + 8G + e.
+// fp32 step (k, e):          slot G    <-> d = 16k + 4G + e.
+// Output s[mt][i] at lane l: key 16mt + 4G + i, column l%16.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__device__ __forceinline__ void qk_tile(const unsigned char* k_lds, const QOps<T, D>& q,
+                                        f32x4 (&s)[KT / 16]) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const int G = lane >> 4;
+  const unsigned char* base = k_lds + (lane & 15) * G_::PITCH + 16 * G;
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::PITCH + 64 * k);
+      if constexpr (T::EB == 2) {
+        acc = mfma_bf16(a, q.v[k], acc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = mfma_f32(__uint_as_float(a[e]), __uint_as_float(q.v[k][e]), acc);
+      }
+    }
+    s[mt] = acc;
+  }
+}
+
+// V^T operand (A) of PV step ks for d-tile dt, bf16: slot 8G+e <-> key
+// 32ks + 4G + e (e < 4) and 32ks + 16 + 4G + (e - 4) (e >= 4), head-dim row
+// 16dt + l%16.  ds_read_b64_tr_b16 turns four 8-byte row pieces of the 16
+// lanes of a group into one column per lane.
+__device__ __forceinline__ u32x4 v_operand_bf16(const unsigned char* v_lds, int pitch, int ks, int dt) {
+  const int lane = lane_id();
+  const int G = lane >> 4;
+  const int j = lane & 15;
+#if PKV_V_TRANSPOSE_READ
+  const unsigned char* p0 = v_lds + (32 * ks + 4 * G + (j >> 2)) * pitch + 2 * (16 * dt + 4 * (j & 3));
+  const unsigned char* p1 = p0 + 16 * pitch;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS i16x4*)(p0));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS i16x4*)(p1));
+  u32x2 a = __builtin_bit_cast(u32x2, lo);
+  u32x2 b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+#else
+  const unsigned char* col = v_lds + 2 * (16 * dt + j);
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int key = 32 * ks + (e < 4 ? 4 * G + e : 16 + 4 * G + (e - 4));
+    h[e] = *reinterpret_cast<const uint16_t*>(col + key * pitch);
+  }
+  return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// One tile of the chunk core for NT column groups.
+//   s        raw QK^T accumulators per column group (from qk_tile), consumed
+//   lim[nt]  this lane's column sees keys < lim (global positions)
+//   j0       global position of the tile's first key
+//   mul      score multiplier (scale, times log2(e) for bf16)
+// Steps per column: mask; tile max (exact); new running max; alpha =
+// exp(m_old - m_new) (0 when nothing was visible yet); p = exp(s - m_new)
+// for visible keys, else 0; bf16: p rounded to bf16 once, and that rounded p
+// is both summed and multiplied into V; l = fma(l, alpha, sum of this lane's
+// p in (mt, i) order); o = o * alpha; o += P V by MFMA in PV-step order.
+// ---------------------------------------------------------------------------
+template <class T, int D, int NT>
+__device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
+                                                const int (&lim)[NT], int j0, float mul,
+                                                const unsigned char* v_lds) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const int G = lane >> 4;
+
+  // P operands: bf16 -> 2 PV steps of 32 keys (packed u32x4); fp32 -> 16 steps (one float each).
+  u32x4 pb[NT][KT / 32];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = j0 + 16 * mt + 4 * G + i;
+        const float x = key < lim[nt] ? s[nt][mt][i] * mul : -INFINITY;
+        s[nt][mt][i] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_old = st.m[nt];
+    const float m_new = fmaxf(m_old, tmax);
+    const float alpha = (m_old == -INFINITY) ? 0.f : pkv_exp<T>(m_old - m_new);
+    float tsum = 0.f;
+    uint32_t bits[KT / 16][4];
+#pragma unroll
+    for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = j0 + 16 * mt + 4 * G + i;
+        float p = key < lim[nt] ? pkv_exp<T>(s[nt][mt][i] - m_new) : 0.f;
+        if constexpr (T::EB == 2) {
+          const uint32_t b = bf16_rne_bits(p);
+          bits[mt][i] = b;
+          p = __uint_as_float(b << 16);
+        }
+        s[nt][mt][i] = p;
+        tsum = tsum + p;
+      }
+    st.l[nt] = fmaf(st.l[nt], alpha, tsum);
+    st.m[nt] = m_new;
+#pragma unroll
+    for (int dt = 0; dt < G_::DT; ++dt) st.o[nt][dt] = st.o[nt][dt] * alpha;
+    if constexpr (T::EB == 2) {
+#pragma unroll
+      for (int ks = 0; ks < KT / 32; ++ks) {
+        pb[nt][ks] = u32x4{bits[2 * ks][0] | (bits[2 * ks][1] << 16), bits[2 * ks][2] | (bits[2 * ks][3] << 16),
+                           bits[2 * ks + 1][0] | (bits[2 * ks + 1][1] << 16),
+                           bits[2 * ks + 1][2] | (bits[2 * ks + 1][3] << 16)};
+      }
+    }
+  }
+
+  if constexpr (T::EB == 2) {
+#pragma unroll
+    for (int dt = 0; dt < G_::DT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < KT / 32; ++ks) {
+        const u32x4 va = v_operand_bf16(v_lds, G_::PITCH, ks, dt);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st.o[nt][dt] = mfma_bf16(va, pb[nt][ks], st.o[nt][dt]);
+      }
+  } else {
+    // fp32 PV step (mt, i): slot G <-> key 16mt + 4G + i.
+    const unsigned char* col = v_lds + 4 * (lane & 15);
+#pragma unroll
+    for (int dt = 0; dt < G_::DT; ++dt)
+#pragma unroll
+      for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float va = *reinterpret_cast<const float*>(col + (16 * mt + 4 * G + i) * G_::PITCH + 4 * 16 * dt);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) st.o[nt][dt] = mfma_f32(va, s[nt][mt][i], st.o[nt][dt]);
+        }
+  }
+}
+
+// Column sum of the per-lane partial l (lanes 16 apart hold the same column):
+// a fixed xor butterfly, so every lane of the column gets the same bits.
+__device__ __forceinline__ float column_sum(float x) {
+  x = x + __shfl_xor(x, 16);
+  x = x + __shfl_xor(x, 32);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// The fold of one chunk result (mc, lc, oc) into a row state (M, L, O), in
+// ascending chunk order.  A chunk with no visible key (mc = -inf) is skipped.
+// ---------------------------------------------------------------------------
+template <class T>
+struct FoldCoef {
+  float mn, a, b;
+};
+
+template <class T>
+__device__ __forceinline__ FoldCoef<T> fold_coef(float M, float mc) {
+  FoldCoef<T> f;
+  f.mn = fmaxf(M, mc);
+  f.a = (M == -INFINITY) ? 0.f : pkv_exp<T>(M - f.mn);
+  f.b = pkv_exp<T>(mc - f.mn);
+  return f;
+}
+__device__ __forceinline__ float fold_val(float acc, float a, float x, float b) { return fmaf(acc, a, x * b); }
+
+// Final write: out = O / L rounded once to the output type; lse in natural log.
+template <class T>
+__device__ __forceinline__ float final_lse(float M, float L) {
+  return M == -INFINITY ? -INFINITY : pkv_lse<T>(M, L);
+}
+__device__ __forceinline__ float final_val(float M, float O, float L) { return M == -INFINITY ? 0.f : O / L; }
+
+}  // namespace pkv

@@ -1,0 +1,100 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/pkv.h
+declares, and rejects bad arguments on the host before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_paged_kv_amd as pkv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_is_built_and_loads():
+    assert os.path.exists(pkv.LIB_PATH), "run python -m invariant_paged_kv_amd.build"
+    L = pkv.lib()
+    assert L.pkv_abi_version() == 1
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(pkv.EXPORTS), (names, pkv.EXPORTS)
+    L = pkv.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def good_layout(**over):
+    lay = pkv.PkvLayout()
+    vals = dict(dtype=pkv.PKV_BF16, batch=2, num_heads_q=16, num_heads_k=4, head_dim=128, block_size=16,
+                max_blocks_per_seq=8, max_seqlen_q=1, max_seqlen_k=0, total_q=2, num_blocks=16,
+                k_block_stride=2 * 16 * 4 * 128, k_slot_stride=4 * 128, k_head_stride=128,
+                v_block_stride=2 * 16 * 4 * 128, v_slot_stride=4 * 128, v_head_stride=128)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(lay, k, v)
+    return lay
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, 0),
+    ({"dtype": 7}, -3),
+    ({"num_heads_q": 6}, -2),
+    ({"num_heads_k": 0}, -2),
+    ({"head_dim": 96}, -2),
+    ({"block_size": 0}, -2),
+    ({"k_slot_stride": 4 * 128 + 4}, -4),        # 8-byte multiple only: breaks 128-bit loads
+    ({"v_head_stride": -128}, -2),
+    ({"dtype": pkv.PKV_F32, "k_head_stride": 132}, 0),
+    ({"dtype": pkv.PKV_F32, "k_head_stride": 130}, -4),
+    ({"max_seqlen_q": -1}, -2),
+])
+def test_validate_layout(over, code):
+    L = pkv.lib()
+    assert L.pkv_validate_layout(ctypes.byref(good_layout(**over))) == code
+    if code:
+        assert L.pkv_last_error().decode()
+
+
+def test_null_and_misaligned_pointers_fail_before_launch():
+    L = pkv.lib()
+    lay = good_layout()
+    rc = L.pkv_attn_forward(None, None, None, ctypes.byref(lay), None, None, None, 1, 0.1, None, None, None)
+    assert rc == -1 and "NULL" in L.pkv_last_error().decode()
+    rc = L.pkv_attn_forward(8, 16, 32, ctypes.byref(lay), 64, 64, 64, 1, 0.1, 48, 64, None)
+    assert rc == -4
+    rc = L.pkv_attn_forward(16, 16, 32, ctypes.byref(lay), 64, 64, 64, 1, float("nan"), 48, 64, None)
+    assert rc == -2
+    rc = L.pkv_cache_write(None, None, None, None, ctypes.byref(lay), None, None, None, 3, None)
+    assert rc == -1
+    rc = L.pkv_attn_forward(16, 16, 32, None, 64, 64, 64, 1, 0.1, 48, 64, None)
+    assert rc == -1
+
+
+def test_workspace_size_matches_partial_buffers():
+    L = pkv.lib()
+    lay = good_layout(max_seqlen_k=4096, total_q=64, batch=64, max_blocks_per_seq=768)
+    chunks = 4096 // pkv.CHUNK_KEYS
+    parts = 64 * 16 * chunks
+    want = -(-parts * 128 * 4 // 256) * 256 + -(-parts * 2 * 4 // 256) * 256
+    assert L.pkv_attn_workspace_size(ctypes.byref(lay)) == want
+    assert L.pkv_attn_workspace_size(ctypes.byref(good_layout(head_dim=3))) == 0
+
+
+def test_options_roundtrip_and_errors():
+    L = pkv.lib()
+    with pkv.options(path=2, split_chunks=3):
+        assert pkv.get_option(pkv.PKV_OPT_PATH) == 2
+        assert pkv.get_option(pkv.PKV_OPT_SPLIT_CHUNKS) == 3
+    assert pkv.get_option(pkv.PKV_OPT_PATH) == 0
+    assert L.pkv_set_option(pkv.PKV_OPT_PATH, 5) == -7
+    assert L.pkv_set_option(99, 0) == -7
+    assert L.pkv_error_string(-4).decode() == "misaligned pointer or stride"
