@@ -189,9 +189,11 @@ __device__ __forceinline__ u32x4 v_operand_bf16(const unsigned char* v_lds, int 
 //   mul      score multiplier (scale, times log2(e) for bf16)
 // Steps per column: mask; tile max (exact); new running max; alpha =
 // exp(m_old - m_new) (0 when nothing was visible yet); p = exp(s - m_new)
-// for visible keys, else 0; bf16: p rounded to bf16 once, and that rounded p
-// is both summed and multiplied into V; l = fma(l, alpha, sum of this lane's
-// p in (mt, i) order); o = o * alpha; o += P V by MFMA in PV-step order.
+// for visible keys, else 0; l = fma(l, alpha, sum of this lane's fp32 p in
+// (mt, i) order); o = o * alpha; o += P V by MFMA in PV-step order, where the
+// bf16 path feeds P to the MFMA rounded once to bf16.  (The row sum uses the
+// unrounded p: summing the rounded values would bias the LSE of short rows by
+// up to 2^-9.)
 // ---------------------------------------------------------------------------
 template <class T, int D, int NT>
 __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
@@ -227,12 +229,8 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = j0 + 16 * mt + 4 * G + i;
-        float p = key < lim[nt] ? pkv_exp<T>(s[nt][mt][i] - m_new) : 0.f;
-        if constexpr (T::EB == 2) {
-          const uint32_t b = bf16_rne_bits(p);
-          bits[mt][i] = b;
-          p = __uint_as_float(b << 16);
-        }
+        const float p = key < lim[nt] ? pkv_exp<T>(s[nt][mt][i] - m_new) : 0.f;
+        if constexpr (T::EB == 2) bits[mt][i] = bf16_rne_bits(p);
         s[nt][mt][i] = p;
         tsum = tsum + p;
       }
