@@ -168,8 +168,10 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
       load_tile<T, D, W>(a, bt, hk, j0, jmax, k_lds, v_lds);
       __syncthreads();
       f32x4 s[NT][KT / 16];
+      KOps<T, D> kop;
+      k_operands_lds<T, D>(k_lds, kop);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(k_lds, q[nt], s[nt]);
+      for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
       softmax_pv_tile<T, D, NT>(st, s, lim, j0, a.mul, v_lds);
     }
 #pragma unroll
@@ -214,16 +216,165 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode split kernel: one wave per work item (sequence, KV head, 16 columns,
+// run of chunks), for up to 16 query columns per KV head (g * L <= 16).
+//
+// Data movement only differs from attn_kernel: each lane loads the K and V
+// pieces it feeds to the MFMAs straight into registers (K row 16mt + l%16,
+// bytes 64k + 16G), one tile ahead of the tile being computed, with the block
+// ids one tile further ahead, so a wave keeps ~32 KiB of HBM reads in flight
+// while it computes.  K goes from registers into the QK MFMAs; V goes through
+// a private LDS tile for the transposing read.  The arithmetic is the shared
+// chunk core, so the bits equal those of the prefill kernel.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+struct TileRegs {
+  KOps<T, D> k;
+  KOps<T, D> v;
+};
+
+__device__ __forceinline__ void tile_block_ids(const int32_t* bt, int bs, int j0, int jlast, int (&ids)[KT / 16]) {
+  const int r = lane_id() & 15;
+#pragma unroll
+  for (int mt = 0; mt < KT / 16; ++mt) {
+    const int j = j0 + 16 * mt + r;
+    ids[mt] = j < jlast ? bt[j / bs] : 0;
+  }
+}
+
+template <class T, int D>
+__device__ __forceinline__ void tile_load_regs(const AttnArgs& a, int hk, int j0, int jlast, const int (&ids)[KT / 16],
+                                               TileRegs<T, D>& r, bool want_k, bool want_v) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const unsigned char* kb = static_cast<const unsigned char*>(a.k);
+  const unsigned char* vb = static_cast<const unsigned char*>(a.v);
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt) {
+    const int j = j0 + 16 * mt + (lane & 15);
+    const bool in = j < jlast;
+    const int64_t blk = ids[mt];
+    const int64_t slot = j % a.bs;
+    const unsigned char* kp = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::EB + 16 * (lane >> 4);
+    const unsigned char* vp = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::EB + 16 * (lane >> 4);
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) {
+      if (want_k) r.k[mt][k] = in ? *reinterpret_cast<const u32x4*>(kp + 64 * k) : u32x4{0, 0, 0, 0};
+      if (want_v) r.v[mt][k] = in ? *reinterpret_cast<const u32x4*>(vp + 64 * k) : u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <class T, int D>
+__device__ __forceinline__ void tile_store_v(unsigned char* v_lds, const TileRegs<T, D>& r) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  unsigned char* base = v_lds + (lane & 15) * G_::PITCH + 16 * (lane >> 4);
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) *reinterpret_cast<u32x4*>(base + mt * 16 * G_::PITCH + 64 * k) = r.v[mt][k];
+}
+
+// Two waves per SIMD (<= 256 registers): 8 waves per CU, each with one tile
+// (32 KiB at d = 128) of K/V loads in flight while it computes the previous one.
+template <class T, int D>
+__global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
+  using G_ = TileGeom<T, D>;
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::BYTES];
+
+  const int b = blockIdx.z;
+  const int hk = blockIdx.y;
+  const int cb = blockIdx.x % a.ncb;
+  const int item = blockIdx.x / a.ncb;
+  const int n = a.seqlens_k[b];
+  const int q0 = a.cu_q[b];
+  const int L = a.cu_q[b + 1] - q0;
+  const int g = a.g;
+  const int ncols = L * g;
+  const int col0 = cb * 16;
+  if (col0 >= ncols) return;
+  const int last_col = min(col0 + 16, ncols) - 1;
+  const int jmax = column_limit(last_col, ncols, g, n, L, a.causal);
+  const int nchunks = jmax > 0 ? (jmax + KC - 1) / KC : 0;
+  const int c_begin = item * a.cpi;
+  const int c_end = min(min(c_begin + a.cpi, nchunks), a.maxc);
+  if (c_begin >= c_end) return;
+  const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
+
+  const int lane = lane_id();
+  const int G = lane >> 4;
+  const int col = col0 + (lane & 15);
+  const int lim[1] = {column_limit(col, ncols, g, n, L, a.causal)};
+  QOps<T, D> q;
+  if (col < ncols) {
+    const int64_t qelem = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * D;
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB + 16 * G;
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + 64 * k);
+  } else {
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) q.v[k] = u32x4{0, 0, 0, 0};
+  }
+
+  const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
+  int j0 = c_begin * KC;
+  int ids[KT / 16];
+  TileRegs<T, D> r;
+  tile_block_ids(bt, a.bs, j0, jlast, ids);
+  tile_load_regs<T, D>(a, hk, j0, jlast, ids, r, true, true);
+  tile_block_ids(bt, a.bs, j0 + KT, jlast, ids);
+
+  // Per tile: copy V(t) to LDS and refill those registers with V(t+1); QK on
+  // K(t) and refill with K(t+1); then softmax + PV(t) while t+1 is in flight.
+  ChunkState<D, 1> st;
+  for (int c = c_begin; c < c_end; ++c) {
+    chunk_reset(st);
+    const int jend = min((c + 1) * KC, jmax);
+    for (; j0 < jend; j0 += KT) {
+      const int jn = j0 + KT;
+      const bool more = jn < jlast;
+      tile_store_v<T, D>(v_lds, r);
+      if (more) tile_load_regs<T, D>(a, hk, jn, jlast, ids, r, false, true);
+      f32x4 s[1][KT / 16];
+      qk_tile<T, D>(r.k, q, s[0]);
+      if (more) {
+        tile_load_regs<T, D>(a, hk, jn, jlast, ids, r, true, false);
+        tile_block_ids(bt, a.bs, jn + KT, jlast, ids);
+      }
+      softmax_pv_tile<T, D, 1, true>(st, s, lim, j0, a.mul, v_lds);
+    }
+    const float lc = column_sum(st.l[0]);
+    if (col < ncols) {
+      const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.maxc + c;
+      if (G == 0) {
+        a.part_ml[2 * idx] = st.m[0];
+        a.part_ml[2 * idx + 1] = lc;
+      }
+      float* po = a.part_o + idx * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * G) = st.o[0][dt];
+    }
+  }
+}
+
+constexpr int kMergeWavesPerRow = 2;
+
 // Fold of one row's chunk partials, ascending chunk index, then the final
-// write.  One wave per (row, query head); lane holds head-dim elements
-// 2*lane, 2*lane+1 (d = 128) or lane (d = 64).
+// write.  WPR waves per (row, query head), each owning D / WPR head-dim
+// elements (EPL per lane); chunk partials are loaded PF chunks ahead of the
+// sequential fold.
 template <class T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int EPL = D / 64;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int WPR = kMergeWavesPerRow;
+  constexpr int EPL = D / 64 / WPR > 0 ? D / 64 / WPR : 1;
+  constexpr int PF = 16;
+  const int64_t wg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t w = wg / WPR;
+  const int part = static_cast<int>(wg % WPR);
   if (w >= a.total_q * a.hq) return;
   const int64_t row = w / a.hq;
-  const int head = static_cast<int>(w % a.hq);
   int lo = 0, hi = a.batch;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -237,32 +388,42 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int lim = a.causal ? min(p + 1, n) : n;
   const int nck = lim > 0 ? min((lim + KC - 1) / KC, a.maxc) : 0;
   const int lane = lane_id();
+  const int e0 = part * (D / WPR) + EPL * lane;
+  const bool active = EPL * lane < D / WPR;
   float M = -INFINITY, Ls = 0.f;
   float O[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) O[e] = 0.f;
   const int64_t base = w * a.maxc;
-  for (int c = 0; c < nck; ++c) {
-    const float mc = a.part_ml[2 * (base + c)];
-    const float lc = a.part_ml[2 * (base + c) + 1];
-    const float* po = a.part_o + (base + c) * D + EPL * lane;
-    float oc[EPL];
+  for (int c0 = 0; c0 < nck; c0 += PF) {
+    float mc[PF], lc[PF], oc[PF][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) oc[e] = po[e];
-    if (mc == -INFINITY) continue;
-    const FoldCoef<T> f = fold_coef<T>(M, mc);
-    Ls = fold_val(Ls, f.a, lc, f.b);
+    for (int i = 0; i < PF; ++i) {
+      const int c = min(c0 + i, nck - 1);
+      mc[i] = a.part_ml[2 * (base + c)];
+      lc[i] = a.part_ml[2 * (base + c) + 1];
+      const float* po = a.part_o + (base + c) * D + e0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) O[e] = fold_val(O[e], f.a, oc[e], f.b);
-    M = f.mn;
+      for (int e = 0; e < EPL; ++e) oc[i][e] = active ? po[e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      if (c0 + i >= nck || mc[i] == -INFINITY) continue;
+      const FoldCoef<T> f = fold_coef<T>(M, mc[i]);
+      Ls = fold_val(Ls, f.a, lc[i], f.b);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) O[e] = fold_val(O[e], f.a, oc[i][e], f.b);
+      M = f.mn;
+    }
   }
-  if (lane == 0) a.lse[w] = final_lse<T>(M, Ls);
+  if (lane == 0 && part == 0) a.lse[w] = final_lse<T>(M, Ls);
+  if (!active) return;
   if constexpr (T::EB == 2) {
-    uint16_t* o = static_cast<uint16_t*>(a.out) + w * D + EPL * lane;
+    uint16_t* o = static_cast<uint16_t*>(a.out) + w * D + e0;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = static_cast<uint16_t>(bf16_rne_bits(final_val(M, O[e], Ls)));
   } else {
-    float* o = static_cast<float*>(a.out) + w * D + EPL * lane;
+    float* o = static_cast<float*>(a.out) + w * D + e0;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = final_val(M, O[e], Ls);
   }
@@ -280,7 +441,11 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   }
   dim3 grid(a.ncb * pl.items, pl.hk, pl.batch);
   if (pl.waves == 1) {
-    hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true>), grid, dim3(64), 0, stream, a);
+    if constexpr (T::EB == 2) {
+      hipLaunchKernelGGL((decode_kernel<T, D>), grid, dim3(64), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true>), grid, dim3(64), 0, stream, a);
+    }
   } else {
     hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, true>), grid, dim3(256), 0, stream, a);
   }
@@ -300,7 +465,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   m.causal = a.causal;
   const int64_t waves = pl.total_q * a.hq;
   if (waves == 0) return hipSuccess;
-  dim3 mgrid(static_cast<unsigned>((waves + 3) / 4));
+  dim3 mgrid(static_cast<unsigned>((waves * kMergeWavesPerRow + 3) / 4));
   hipLaunchKernelGGL((merge_kernel<T, D>), mgrid, dim3(256), 0, stream, m);
   return hipGetLastError();
 }

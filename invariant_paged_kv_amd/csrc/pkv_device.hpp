@@ -123,34 +123,47 @@ struct QOps {
 
 // ---------------------------------------------------------------------------
 // QK^T for one tile: S^T[key][col] = sum over d of K[key][d] * Q[col][d].
-// K (A operand) comes from the LDS tile; Q (B operand) from registers.
+// K operands (A): kop[mt][k] at lane l holds bytes [64k + 16G, +16) of key row
+// 16mt + l%16 of the tile (G = l/16); Q operands (B) come from QOps.
 // bf16 k-slot map of step k: slot 8G+e <-> d = 32k + 8G + e.
 // fp32 step (k, e):          slot G    <-> d = 16k + 4G + e.
+// The MFMA chain runs k (then e) in ascending order from a zero accumulator.
 // Output s[mt][i] at lane l: key 16mt + 4G + i, column l%16.
 // ---------------------------------------------------------------------------
 template <class T, int D>
-__device__ __forceinline__ void qk_tile(const unsigned char* k_lds, const QOps<T, D>& q,
-                                        f32x4 (&s)[KT / 16]) {
+using KOps = u32x4[KT / 16][TileGeom<T, D>::NK];
+
+template <class T, int D>
+__device__ __forceinline__ void qk_tile(const KOps<T, D>& kop, const QOps<T, D>& q, f32x4 (&s)[KT / 16]) {
   using G_ = TileGeom<T, D>;
-  const int lane = lane_id();
-  const int G = lane >> 4;
-  const unsigned char* base = k_lds + (lane & 15) * G_::PITCH + 16 * G;
 #pragma unroll
   for (int mt = 0; mt < G_::MT; ++mt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::PITCH + 64 * k);
       if constexpr (T::EB == 2) {
-        acc = mfma_bf16(a, q.v[k], acc);
+        acc = mfma_bf16(kop[mt][k], q.v[k], acc);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc = mfma_f32(__uint_as_float(a[e]), __uint_as_float(q.v[k][e]), acc);
+          acc = mfma_f32(__uint_as_float(kop[mt][k][e]), __uint_as_float(q.v[k][e]), acc);
       }
     }
     s[mt] = acc;
   }
+}
+
+// K operands of a tile staged row-major in LDS (row pitch G_::PITCH).
+template <class T, int D>
+__device__ __forceinline__ void k_operands_lds(const unsigned char* k_lds, KOps<T, D>& kop) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const unsigned char* base = k_lds + (lane & 15) * G_::PITCH + 16 * (lane >> 4);
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k)
+      kop[mt][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::PITCH + 64 * k);
 }
 
 // V^T operand (A) of PV step ks for d-tile dt, bf16: slot 8G+e <-> key
@@ -195,7 +208,7 @@ __device__ __forceinline__ u32x4 v_operand_bf16(const unsigned char* v_lds, int 
 // unrounded p: summing the rounded values would bias the LSE of short rows by
 // up to 2^-9.)
 // ---------------------------------------------------------------------------
-template <class T, int D, int NT>
+template <class T, int D, int NT, bool kPinVReads = false>
 __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
                                                 const int (&lim)[NT], int j0, float mul,
                                                 const unsigned char* v_lds) {
@@ -250,13 +263,18 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
 
   if constexpr (T::EB == 2) {
 #pragma unroll
-    for (int dt = 0; dt < G_::DT; ++dt)
+    for (int dt = 0; dt < G_::DT; ++dt) {
 #pragma unroll
       for (int ks = 0; ks < KT / 32; ++ks) {
         const u32x4 va = v_operand_bf16(v_lds, G_::PITCH, ks, dt);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) st.o[nt][dt] = mfma_bf16(va, pb[nt][ks], st.o[nt][dt]);
       }
+      // Optionally keep each d-tile's V operand reads next to its MFMAs, so the
+      // scheduler cannot hoist all of them (caps live registers; no effect on
+      // the arithmetic).
+      if constexpr (kPinVReads) __builtin_amdgcn_sched_barrier(0);
+    }
   } else {
     // fp32 PV step (mt, i): slot G <-> key 16mt + 4G + i.
     const unsigned char* col = v_lds + 4 * (lane & 15);
