@@ -182,6 +182,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.causal = causal ? 1 : 0;
   a.mul = l->dtype == PKV_BF16 ? static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634074)
                                : softmax_scale;
+  pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
   hipError_t e = pkv::launch_attention(a, p.lp, l->dtype, l->head_dim, stream);
   if (allocated) {
     hipError_t fe = hipFreeAsync(ws, stream);
@@ -248,6 +249,7 @@ int pkv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v
   a.bs = l->block_size;
   a.mbps = l->max_blocks_per_seq;
   a.row_bytes = l->head_dim * elem_bytes(l->dtype);
+  pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
   hipError_t e = pkv::launch_cache_write(a, elem_bytes(l->dtype), total_new, stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "cache_write launch failed: %s", hipGetErrorString(e));
   return ok();

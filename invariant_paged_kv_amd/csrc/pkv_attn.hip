@@ -43,22 +43,22 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
       const int qi = threadIdx.x + (r0 + i) * 64 * W;
       const int row = qi / G_::CPR, part = qi % G_::CPR;
       const int j = j0 + row;
-      if (j < jmax) {
-        const int64_t blk = bt[j / a.bs];
-        const int64_t slot = j % a.bs;
-        kr[i] = *reinterpret_cast<const u32x4*>(kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::EB + 16 * part);
-        vr[i] = *reinterpret_cast<const u32x4*>(vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::EB + 16 * part);
-      } else {
-        kr[i] = u32x4{0, 0, 0, 0};
-        vr[i] = u32x4{0, 0, 0, 0};
-      }
+      const int jc = min(j, jmax - 1);  // rows past jmax load a visible row, then read as zero
+      const int bi = div_block(jc, a.bs_mul, a.bs_shift);
+      const int64_t blk = bt[bi];
+      const int64_t slot = jc - bi * a.bs;
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::EB + 16 * part);
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::EB + 16 * part);
+      const bool in = j < jmax;
+      kr[i] = in ? kv : u32x4{0, 0, 0, 0};
+      vr[i] = in ? vv : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int qi = threadIdx.x + (r0 + i) * 64 * W;
       const int row = qi / G_::CPR, part = qi % G_::CPR;
-      *reinterpret_cast<u32x4*>(k_lds + row * G_::PITCH + 16 * part) = kr[i];
-      *reinterpret_cast<u32x4*>(v_lds + row * G_::PITCH + 16 * part) = vr[i];
+      *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = kr[i];
+      *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = vr[i];
     }
   }
 }
@@ -67,7 +67,7 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
 // row-major over (row r, head-in-group hh): col = r * g + hh.  Row r sits at
 // key position n - L + r (bottom-right alignment).
 __device__ __forceinline__ int column_limit(int col, int ncols, int g, int n, int L, int causal) {
-  if (col >= ncols) return 0;
+  if (col >= ncols) return INT_MAX;  // no such column: its values are never stored
   const int p = n - L + col / g;
   return causal ? min(p + 1, n) : n;
 }
@@ -93,9 +93,9 @@ template <class T, int D, int W, int NT, bool SPLIT>
 __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   constexpr int COLS = W * NT * 16;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * G_::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[G_::BYTES];
   unsigned char* k_lds = lds;
-  unsigned char* v_lds = lds + G_::BYTES;
+  unsigned char* v_lds = lds + G_::KBYTES;
 
   const int b = blockIdx.z;
   const int hk = blockIdx.y;
@@ -234,12 +234,15 @@ struct TileRegs {
   KOps<T, D> v;
 };
 
-__device__ __forceinline__ void tile_block_ids(const int32_t* bt, int bs, int j0, int jlast, int (&ids)[KT / 16]) {
+// Block ids of this lane's four tile rows (rows past jlast use the last
+// visible row's block, so every read stays inside the sequence's blocks).
+__device__ __forceinline__ void tile_block_ids(const AttnArgs& a, const int32_t* bt, int j0, int jlast,
+                                               int (&ids)[KT / 16]) {
   const int r = lane_id() & 15;
 #pragma unroll
   for (int mt = 0; mt < KT / 16; ++mt) {
-    const int j = j0 + 16 * mt + r;
-    ids[mt] = j < jlast ? bt[j / bs] : 0;
+    const int j = min(j0 + 16 * mt + r, jlast - 1);
+    ids[mt] = bt[div_block(j, a.bs_mul, a.bs_shift)];
   }
 }
 
@@ -254,14 +257,21 @@ __device__ __forceinline__ void tile_load_regs(const AttnArgs& a, int hk, int j0
   for (int mt = 0; mt < G_::MT; ++mt) {
     const int j = j0 + 16 * mt + (lane & 15);
     const bool in = j < jlast;
+    const int jc = min(j, jlast - 1);  // rows past jlast load a visible row, then read as zero
     const int64_t blk = ids[mt];
-    const int64_t slot = j % a.bs;
+    const int64_t slot = jc - div_block(jc, a.bs_mul, a.bs_shift) * a.bs;
     const unsigned char* kp = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::EB + 16 * (lane >> 4);
     const unsigned char* vp = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::EB + 16 * (lane >> 4);
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) {
-      if (want_k) r.k[mt][k] = in ? *reinterpret_cast<const u32x4*>(kp + 64 * k) : u32x4{0, 0, 0, 0};
-      if (want_v) r.v[mt][k] = in ? *reinterpret_cast<const u32x4*>(vp + 64 * k) : u32x4{0, 0, 0, 0};
+      if (want_k) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(kp + 64 * k);
+        r.k[mt][k] = in ? x : u32x4{0, 0, 0, 0};
+      }
+      if (want_v) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(vp + 64 * k);
+        r.v[mt][k] = in ? x : u32x4{0, 0, 0, 0};
+      }
     }
   }
 }
@@ -270,11 +280,212 @@ template <class T, int D>
 __device__ __forceinline__ void tile_store_v(unsigned char* v_lds, const TileRegs<T, D>& r) {
   using G_ = TileGeom<T, D>;
   const int lane = lane_id();
-  unsigned char* base = v_lds + (lane & 15) * G_::PITCH + 16 * (lane >> 4);
+  unsigned char* base = v_lds + (lane & 15) * G_::VPITCH + 16 * (lane >> 4);
 #pragma unroll
   for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
-    for (int k = 0; k < G_::NK; ++k) *reinterpret_cast<u32x4*>(base + mt * 16 * G_::PITCH + 64 * k) = r.v[mt][k];
+    for (int k = 0; k < G_::NK; ++k) *reinterpret_cast<u32x4*>(base + mt * 16 * G_::VPITCH + 64 * k) = r.v[mt][k];
+}
+
+#ifndef PKV_PF_XCD
+#define PKV_PF_XCD 1
+#endif
+// ---------------------------------------------------------------------------
+// Prefill kernel: one work group of W waves per (sequence, KV head, W*16
+// columns); every wave owns 16 columns (one MFMA N tile) and runs the chunk
+// core over all chunks in ascending order, folding each chunk result into its
+// row state in registers, then writes out/lse.  K/V tiles are staged in LDS
+// by all W*64 threads and shared by the W waves (one HBM read serves the
+// whole GQA group); the LDS tiles are double-buffered and the next tile's
+// global loads are issued before the current tile is computed.
+// ---------------------------------------------------------------------------
+template <class T, int D, int W>
+struct PrefillStage {
+  static constexpr int NCH = KT * TileGeom<T, D>::CPR;  // 16-byte pieces per tensor per tile
+  static constexpr int PER = NCH / (64 * W);
+  u32x4 k[PER];
+  u32x4 v[PER];
+};
+
+template <class T, int D, int W>
+__device__ __forceinline__ void prefill_load(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
+                                             PrefillStage<T, D, W>& r) {
+  using G_ = TileGeom<T, D>;
+  using S_ = PrefillStage<T, D, W>;
+  static_assert(S_::PER * 64 * W == S_::NCH, "tile pieces must split evenly over the work group");
+  const unsigned char* kb = static_cast<const unsigned char*>(a.k);
+  const unsigned char* vb = static_cast<const unsigned char*>(a.v);
+#pragma unroll
+  for (int i = 0; i < S_::PER; ++i) {
+    const int qi = threadIdx.x + i * 64 * W;
+    const int row = qi / G_::CPR, part = qi % G_::CPR;
+    const int j = j0 + row;
+    const int jc = min(j, jmax - 1);  // rows past jmax load a visible row, then read as zero
+    const int bi = div_block(jc, a.bs_mul, a.bs_shift);
+    const int64_t blk = bt[bi];
+    const int64_t slot = jc - bi * a.bs;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::EB + 16 * part);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::EB + 16 * part);
+    const bool in = j < jmax;
+    r.k[i] = in ? kv : u32x4{0, 0, 0, 0};
+    r.v[i] = in ? vv : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <class T, int D, int W>
+__device__ __forceinline__ void prefill_store(unsigned char* k_lds, unsigned char* v_lds, const PrefillStage<T, D, W>& r) {
+  using G_ = TileGeom<T, D>;
+  using S_ = PrefillStage<T, D, W>;
+#pragma unroll
+  for (int i = 0; i < S_::PER; ++i) {
+    const int qi = threadIdx.x + i * 64 * W;
+    const int row = qi / G_::CPR, part = qi % G_::CPR;
+    *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = r.k[i];
+    *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = r.v[i];
+  }
+}
+
+// QK^T with the K operands read from the LDS tile one M tile at a time (same
+// MFMA chain as qk_tile).
+template <class T, int D>
+__device__ __forceinline__ void qk_tile_lds(const unsigned char* k_lds, const QOps<T, D>& q, f32x4 (&s)[KT / 16]) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH + 16 * (lane >> 4);
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt) {
+    KOps<T, D> kop;
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) kop[0][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + 64 * k);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) {
+      if constexpr (T::EB == 2) {
+        acc = mfma_bf16(kop[0][k], q.v[k], acc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = mfma_f32(__uint_as_float(kop[0][k][e]), __uint_as_float(q.v[k][e]), acc);
+      }
+    }
+    s[mt] = acc;
+  }
+}
+
+// One prefill tile: `cur` is refilled with tile t+2 while tile t is computed
+// from LDS buffer t&1; `nxt` (tile t+1) goes to LDS buffer (t+1)&1 afterwards.
+template <class T, int D, int W>
+__device__ __forceinline__ void prefill_tile(const AttnArgs& a, const int32_t* bt, int hk, int t, int ntiles, int jmax,
+                                             unsigned char* lds, PrefillStage<T, D, W>& cur,
+                                             PrefillStage<T, D, W>& nxt, const QOps<T, D>& q, const int (&lim)[1],
+                                             ChunkState<D, 1>& st, float& M, float& Ls, f32x4 (&O)[D / 16]) {
+  using G_ = TileGeom<T, D>;
+  const int j0 = t * KT;
+  if (t + 2 < ntiles) prefill_load<T, D, W>(a, bt, hk, j0 + 2 * KT, jmax, cur);
+  const unsigned char* k_lds = lds + (t & 1) * G_::BYTES;
+  f32x4 s[1][KT / 16];
+  qk_tile_lds<T, D>(k_lds, q, s[0]);
+  softmax_pv_tile<T, D, 1, true>(st, s, lim, j0, a.mul, k_lds + G_::KBYTES);
+  // chunk end: fold the chunk result into the row state
+  if ((j0 + KT) % KC == 0 || t + 1 == ntiles) {
+    const float lc = column_sum(st.l[0]);
+    if (st.m[0] != -INFINITY) {
+      const FoldCoef<T> f = fold_coef<T>(M, st.m[0]);
+      Ls = fold_val(Ls, f.a, lc, f.b);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[dt][i] = fold_val(O[dt][i], f.a, st.o[0][dt][i], f.b);
+      M = f.mn;
+    }
+    chunk_reset(st);
+  }
+  if (t + 1 < ntiles) {
+    unsigned char* nb = lds + ((t + 1) & 1) * G_::BYTES;
+    prefill_store<T, D, W>(nb, nb + G_::KBYTES, nxt);
+  }
+  __syncthreads();
+}
+
+template <class T, int D, int W>
+__global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
+  using G_ = TileGeom<T, D>;
+  constexpr int COLS = W * 16;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * G_::BYTES];  // 2 x (K, V)
+
+#if PKV_PF_XCD
+  // Work groups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2); renumber them so that one XCD runs consecutive column blocks of the
+  // same (sequence, KV head) and its L2 serves their shared K/V tiles.
+  const int nwg = gridDim.x * gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int full8 = nwg / 8 * 8;
+  const int w = lin < full8 ? (lin % 8) * (nwg / 8) + lin / 8 : lin;
+  const int b = w / (gridDim.x * gridDim.y);
+  const int hk = (w / gridDim.x) % gridDim.y;
+  const int cb = a.ncb - 1 - w % gridDim.x;  // heaviest causal blocks first
+#else
+  const int b = blockIdx.z;
+  const int hk = blockIdx.y;
+  const int cb = a.ncb - 1 - static_cast<int>(blockIdx.x);  // heaviest causal blocks first
+#endif
+  const int n = a.seqlens_k[b];
+  const int q0 = a.cu_q[b];
+  const int L = a.cu_q[b + 1] - q0;
+  const int g = a.g;
+  const int ncols = L * g;
+  const int col0 = cb * COLS;
+  if (col0 >= ncols) return;
+  const int last_col = min(col0 + COLS, ncols) - 1;
+  const int jmax = column_limit(last_col, ncols, g, n, L, a.causal);
+  const int ntiles = jmax > 0 ? (jmax + KT - 1) / KT : 0;
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int G = lane >> 4;
+  const int col = col0 + wave * 16 + (lane & 15);
+  const int lim[1] = {column_limit(col, ncols, g, n, L, a.causal)};
+  QOps<T, D> q;
+  if (col < ncols) {
+    const int64_t qelem = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * D;
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB + 16 * G;
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + 64 * k);
+  } else {
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) q.v[k] = u32x4{0, 0, 0, 0};
+  }
+
+  float M = -INFINITY, Ls = 0.f;
+  f32x4 O[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
+  // Tile t is computed from LDS buffer t&1 while one register stage holds tile
+  // t+1 (loaded during tile t-1) and the other receives tile t+2.
+  PrefillStage<T, D, W> sa, sb;
+  if (ntiles > 0) {
+    prefill_load<T, D, W>(a, bt, hk, 0, jmax, sa);
+    if (ntiles > 1) prefill_load<T, D, W>(a, bt, hk, KT, jmax, sb);
+    prefill_store<T, D, W>(lds, lds + G_::KBYTES, sa);
+  }
+  __syncthreads();
+  ChunkState<D, 1> st;
+  chunk_reset(st);
+  for (int t = 0; t < ntiles; ++t) {
+    if ((t & 1) == 0) {
+      prefill_tile<T, D, W>(a, bt, hk, t, ntiles, jmax, lds, sa, sb, q, lim, st, M, Ls, O);
+    } else {
+      prefill_tile<T, D, W>(a, bt, hk, t, ntiles, jmax, lds, sb, sa, q, lim, st, M, Ls, O);
+    }
+  }
+
+  if (col < ncols) {
+    const int64_t rh = (int64_t)(q0 + col / g) * a.hq + hk * g + col % g;
+    if (G == 0) a.lse[rh] = final_lse<T>(M, Ls);
+    store_out<T, D>(a.out, rh * D, O, M, Ls);
+  }
 }
 
 // Two waves per SIMD (<= 256 registers): 8 waves per CU, each with one tile
@@ -282,7 +493,7 @@ __device__ __forceinline__ void tile_store_v(unsigned char* v_lds, const TileReg
 template <class T, int D>
 __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
 
   const int b = blockIdx.z;
   const int hk = blockIdx.y;
@@ -322,9 +533,9 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   int j0 = c_begin * KC;
   int ids[KT / 16];
   TileRegs<T, D> r;
-  tile_block_ids(bt, a.bs, j0, jlast, ids);
+  tile_block_ids(a, bt, j0, jlast, ids);
   tile_load_regs<T, D>(a, hk, j0, jlast, ids, r, true, true);
-  tile_block_ids(bt, a.bs, j0 + KT, jlast, ids);
+  tile_block_ids(a, bt, j0 + KT, jlast, ids);
 
   // Per tile: copy V(t) to LDS and refill those registers with V(t+1); QK on
   // K(t) and refill with K(t+1); then softmax + PV(t) while t+1 is in flight.
@@ -341,9 +552,9 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
       qk_tile<T, D>(r.k, q, s[0]);
       if (more) {
         tile_load_regs<T, D>(a, hk, jn, jlast, ids, r, true, false);
-        tile_block_ids(bt, a.bs, jn + KT, jlast, ids);
+        tile_block_ids(a, bt, jn + KT, jlast, ids);
       }
-      softmax_pv_tile<T, D, 1, true>(st, s, lim, j0, a.mul, v_lds);
+      softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
     }
     const float lc = column_sum(st.l[0]);
     if (col < ncols) {
@@ -359,7 +570,13 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   }
 }
 
-constexpr int kMergeWavesPerRow = 2;
+#ifndef PKV_MERGE_WPR_EXP
+#define PKV_MERGE_WPR_EXP 2
+#endif
+#ifndef PKV_MERGE_PF_EXP
+#define PKV_MERGE_PF_EXP 16
+#endif
+constexpr int kMergeWavesPerRow = PKV_MERGE_WPR_EXP;
 
 // Fold of one row's chunk partials, ascending chunk index, then the final
 // write.  WPR waves per (row, query head), each owning D / WPR head-dim
@@ -369,7 +586,7 @@ template <class T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int WPR = kMergeWavesPerRow;
   constexpr int EPL = D / 64 / WPR > 0 ? D / 64 / WPR : 1;
-  constexpr int PF = 16;
+  constexpr int PF = PKV_MERGE_PF_EXP;
   const int64_t wg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t w = wg / WPR;
   const int part = static_cast<int>(wg % WPR);
@@ -436,7 +653,11 @@ template <class T, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStream_t stream) {
   if (pl.full) {
     dim3 grid(a.ncb, pl.hk, pl.batch);
-    hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false>), grid, dim3(256), 0, stream, a);
+    if constexpr (T::EB == 2) {
+      hipLaunchKernelGGL((prefill_kernel<T, D, 8>), grid, dim3(512), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
   }
   dim3 grid(a.ncb * pl.items, pl.hk, pl.batch);

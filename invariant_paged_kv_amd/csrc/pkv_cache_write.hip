@@ -24,9 +24,10 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int 
   }
   const int b = lo;
   if (b >= a.batch) return;
-  const int64_t pos = a.seqlens_k[b] + (tok - a.cu_new[b]);
-  const int64_t blk = a.block_table[(int64_t)b * a.mbps + pos / a.bs];
-  const int64_t slot = pos % a.bs;
+  const int pos = a.seqlens_k[b] + static_cast<int>(tok - a.cu_new[b]);
+  const int bi = div_block(pos, a.bs_mul, a.bs_shift);
+  const int64_t blk = a.block_table[(int64_t)b * a.mbps + bi];
+  const int64_t slot = pos - bi * a.bs;
   const int cpr = a.row_bytes / 16;
   const int per_tensor = a.hk * cpr;
   for (int i = threadIdx.x; i < 2 * per_tensor; i += blockDim.x) {

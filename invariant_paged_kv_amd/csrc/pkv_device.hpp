@@ -25,6 +25,7 @@ constexpr int KC = 512;  // keys per chunk (unit of split partials and of the fo
 static_assert(KC % KT == 0, "a chunk is a whole number of tiles");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -79,12 +80,19 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 // LDS tiles.  A tile holds KT consecutive keys (tile-local row = key - j0) of
 // one KV head, row-major with a 16-byte pad per row.
 // ---------------------------------------------------------------------------
+// Row pitches are chosen for the LDS banks: K rows are read 16 bytes per lane
+// from 16 consecutive rows (a 16-byte pad spreads 8 rows over all banks); V
+// rows are read by ds_read_b64_tr_b16, 4 rows x 32 bytes per 16 lanes (a
+// 32-byte pad puts those 4 rows on disjoint banks).
 template <class T, int D>
 struct TileGeom {
   static constexpr int ROW_BYTES = D * T::EB;          // 256 for bf16 d=128
-  static constexpr int PITCH = ROW_BYTES + 16;         // bytes between rows in LDS
+  static constexpr int KPITCH = ROW_BYTES + 16;        // bytes between K rows in LDS
+  static constexpr int VPITCH = ROW_BYTES + 32;        // bytes between V rows in LDS
   static constexpr int CPR = ROW_BYTES / 16;           // 16-byte chunks per row
-  static constexpr int BYTES = KT * PITCH;             // one tensor's tile
+  static constexpr int KBYTES = KT * KPITCH;           // K tile
+  static constexpr int VBYTES = KT * VPITCH;           // V tile
+  static constexpr int BYTES = KBYTES + VBYTES;        // K + V tile
   static constexpr int NK = ROW_BYTES / 64;            // 64-byte column groups (QK steps)
   static constexpr int DT = D / 16;                    // PV output d-tiles
   static constexpr int MT = KT / 16;                   // 16-key M tiles per tile
@@ -153,17 +161,17 @@ __device__ __forceinline__ void qk_tile(const KOps<T, D>& kop, const QOps<T, D>&
   }
 }
 
-// K operands of a tile staged row-major in LDS (row pitch G_::PITCH).
+// K operands of a tile staged row-major in LDS (row pitch G_::KPITCH).
 template <class T, int D>
 __device__ __forceinline__ void k_operands_lds(const unsigned char* k_lds, KOps<T, D>& kop) {
   using G_ = TileGeom<T, D>;
   const int lane = lane_id();
-  const unsigned char* base = k_lds + (lane & 15) * G_::PITCH + 16 * (lane >> 4);
+  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH + 16 * (lane >> 4);
 #pragma unroll
   for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k)
-      kop[mt][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::PITCH + 64 * k);
+      kop[mt][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + 64 * k);
 }
 
 // V^T operand (A) of PV step ks for d-tile dt, bf16: slot 8G+e <-> key
@@ -197,18 +205,23 @@ __device__ __forceinline__ u32x4 v_operand_bf16(const unsigned char* v_lds, int 
 // ---------------------------------------------------------------------------
 // One tile of the chunk core for NT column groups.
 //   s        raw QK^T accumulators per column group (from qk_tile), consumed
-//   lim[nt]  this lane's column sees keys < lim (global positions)
+//   lim[nt]  this lane's column sees keys < lim (global positions); columns
+//            that do not exist carry lim = INT_MAX (their values are never
+//            stored)
 //   j0       global position of the tile's first key
 //   mul      score multiplier (scale, times log2(e) for bf16)
-// Steps per column: mask; tile max (exact); new running max; alpha =
-// exp(m_old - m_new) (0 when nothing was visible yet); p = exp(s - m_new)
-// for visible keys, else 0; l = fma(l, alpha, sum of this lane's fp32 p in
-// (mt, i) order); o = o * alpha; o += P V by MFMA in PV-step order, where the
-// bf16 path feeds P to the MFMA rounded once to bf16.  (The row sum uses the
-// unrounded p: summing the rounded values would bias the LSE of short rows by
-// up to 2^-9.)
+// Steps per column: x = s * mul, masked to -inf for invisible keys; tile max
+// (exact); new running max m_new; alpha = exp(m_old - m_new) (0 when nothing
+// was visible yet); p = exp(x - m_new) (exactly 0 for invisible keys); l =
+// fma(l, alpha, sum of this lane's fp32 p in (mt, i) order); o = o * alpha;
+// o += P V by MFMA in PV-step order, where the bf16 path feeds P to the MFMA
+// rounded once to bf16 (v_cvt_pk_bf16_f32, round to nearest even).  The row
+// sum uses the unrounded p: summing the rounded values would bias the LSE of
+// short rows by up to 2^-9.
+// One shortcut (kShortcuts) changes no bit: when every column of the wave sees
+// the whole tile, the per-key mask is skipped (it would select nothing).
 // ---------------------------------------------------------------------------
-template <class T, int D, int NT, bool kPinVReads = false>
+template <class T, int D, int NT, bool kPinVReads = false, bool kShortcuts = true>
 __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
                                                 const int (&lim)[NT], int j0, float mul,
                                                 const unsigned char* v_lds) {
@@ -216,34 +229,44 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
   const int lane = lane_id();
   const int G = lane >> 4;
 
-  // P operands: bf16 -> 2 PV steps of 32 keys (packed u32x4); fp32 -> 16 steps (one float each).
+  // P operands: bf16 -> 2 PV steps of 32 keys (packed u32x4); fp32 -> s itself.
   u32x4 pb[NT][KT / 32];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    const bool whole = kShortcuts && __all(j0 + KT <= lim[nt]);
     float tmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = j0 + 16 * mt + 4 * G + i;
-        const float x = key < lim[nt] ? s[nt][mt][i] * mul : -INFINITY;
-        s[nt][mt][i] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int i = 0; i < 4; ++i) s[nt][mt][i] = s[nt][mt][i] * mul;
+    if (!whole) {
+#pragma unroll
+      for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j0 + 16 * mt + 4 * G + i;
+          if (key >= lim[nt]) s[nt][mt][i] = -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[nt][mt][i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_old = st.m[nt];
     const float m_new = fmaxf(m_old, tmax);
     const float alpha = (m_old == -INFINITY) ? 0.f : pkv_exp<T>(m_old - m_new);
+    // Invisible keys hold -inf, so exp gives exactly 0 once the column has a
+    // finite max; a column with nothing visible yet subtracts 0 instead of
+    // -inf (its p are all exp(-inf) = 0).
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
     float tsum = 0.f;
-    uint32_t bits[KT / 16][4];
 #pragma unroll
     for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = j0 + 16 * mt + 4 * G + i;
-        const float p = key < lim[nt] ? pkv_exp<T>(s[nt][mt][i] - m_new) : 0.f;
-        if constexpr (T::EB == 2) bits[mt][i] = bf16_rne_bits(p);
+        const float p = pkv_exp<T>(s[nt][mt][i] - m_ref);
         s[nt][mt][i] = p;
         tsum = tsum + p;
       }
@@ -254,9 +277,14 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
     if constexpr (T::EB == 2) {
 #pragma unroll
       for (int ks = 0; ks < KT / 32; ++ks) {
-        pb[nt][ks] = u32x4{bits[2 * ks][0] | (bits[2 * ks][1] << 16), bits[2 * ks][2] | (bits[2 * ks][3] << 16),
-                           bits[2 * ks + 1][0] | (bits[2 * ks + 1][1] << 16),
-                           bits[2 * ks + 1][2] | (bits[2 * ks + 1][3] << 16)};
+        const f32x4 a = s[nt][2 * ks];
+        const f32x4 b = s[nt][2 * ks + 1];
+        const bf16x2 p0 = {(__bf16)a[0], (__bf16)a[1]};
+        const bf16x2 p1 = {(__bf16)a[2], (__bf16)a[3]};
+        const bf16x2 p2 = {(__bf16)b[0], (__bf16)b[1]};
+        const bf16x2 p3 = {(__bf16)b[2], (__bf16)b[3]};
+        pb[nt][ks] = u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
       }
     }
   }
@@ -266,7 +294,7 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
     for (int dt = 0; dt < G_::DT; ++dt) {
 #pragma unroll
       for (int ks = 0; ks < KT / 32; ++ks) {
-        const u32x4 va = v_operand_bf16(v_lds, G_::PITCH, ks, dt);
+        const u32x4 va = v_operand_bf16(v_lds, G_::VPITCH, ks, dt);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) st.o[nt][dt] = mfma_bf16(va, pb[nt][ks], st.o[nt][dt]);
       }
@@ -284,7 +312,7 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
       for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float va = *reinterpret_cast<const float*>(col + (16 * mt + 4 * G + i) * G_::PITCH + 4 * 16 * dt);
+          const float va = *reinterpret_cast<const float*>(col + (16 * mt + 4 * G + i) * G_::VPITCH + 4 * 16 * dt);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) st.o[nt][dt] = mfma_f32(va, s[nt][mt][i], st.o[nt][dt]);
         }

@@ -26,6 +26,8 @@ struct AttnArgs {
   int32_t cpi;     // chunks per split work item
   int32_t causal;
   float mul;       // score multiplier: scale (fp32) or scale*log2(e) (bf16)
+  uint32_t bs_mul; // j / bs == (j * bs_mul) >> bs_shift for 0 <= j < 2^30
+  int32_t bs_shift;
 };
 
 struct MergeArgs {
@@ -57,7 +59,25 @@ struct CacheWriteArgs {
   const int32_t* cu_new;
   int64_t kbs, kss, khs, vbs, vss, vhs;
   int32_t batch, hk, bs, mbps, row_bytes;
+  uint32_t bs_mul;
+  int32_t bs_shift;
 };
+
+// Division by the block size as a multiply and shift: with l = ceil(log2 bs),
+// s = 30 + l and m = ceil(2^s / bs), floor(j / bs) == (j * m) >> s for every
+// 0 <= j < 2^30 (m*bs = 2^s + e with 0 <= e < bs, so the error term
+// j*e / (bs * 2^s) < 2^-l <= 1/bs never crosses an integer), and m < 2^32.
+inline void block_size_divisor(int32_t bs, uint32_t* mul, int32_t* shift) {
+  int l = 0;
+  while ((int64_t{1} << l) < bs) ++l;
+  const int s = 30 + l;
+  *mul = static_cast<uint32_t>(((uint64_t{1} << s) + static_cast<uint64_t>(bs) - 1) / static_cast<uint64_t>(bs));
+  *shift = s;
+}
+
+__device__ __forceinline__ int div_block(int j, uint32_t mul, int shift) {
+  return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(j)) * mul) >> shift);
+}
 
 hipError_t launch_attention(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, int elem_bytes, int64_t total_new, hipStream_t stream);
