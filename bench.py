@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_c5_traffic.json")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -132,7 +133,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "kernel": "pkv_attn_forward (split + merge)",
             "avg_ms": round(attn_avg_ms, 4),
             "bytes_per_launch": attn_bytes,
@@ -147,6 +148,29 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per attention call from the committed rocprofv3 counter summary.
+
+    The counters (FETCH_SIZE, WRITE_SIZE, calibrated on a plain copy) were
+    taken on specific kernel sources; if those have changed since, the figure
+    no longer describes this build and None is reported.
+    """
+    import hashlib
+    try:
+        info = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in info.get("source_files", []):
+        try:
+            h.update(open(os.path.join(ROOT, "invariant_paged_kv_amd", "csrc", f), "rb").read())
+        except OSError:
+            return None
+    if h.hexdigest() != info.get("source_sha256"):
+        return None
+    return info.get("traffic_bytes_per_launch")
 
 
 def bench_prefill(torch, pkv, gen, reps: int = 3):
