@@ -121,7 +121,7 @@ typedef struct pkv_layout {
  *                of this call's own query rows
  *   cu_seqlens_q device int32 [batch + 1], non-decreasing, cu_seqlens_q[0] = 0
  *   causal       nonzero: row at position p sees keys <= p
- *   softmax_scale  multiplies <q, k> (e.g. 1/sqrt(d))
+ *   softmax_scale  multiplies <q, k> (e.g. 1/sqrt(d)); finite and > 0
  *   out          device, [total_q, Hq, d] of dtype (written)
  *   lse          device fp32 [total_q, Hq] (written): natural-log LSE
  *   stream       HIP stream; all work is enqueued there
@@ -131,7 +131,8 @@ typedef struct pkv_layout {
  * max_seqlen_q; cache values at visible positions finite.  The split (decode)
  * path needs a workspace; this entry point takes it from the stream-ordered
  * allocator (hipMallocAsync / hipFreeAsync on `stream`).
- * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_ALIGN (q, caches,
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (also softmax_scale <= 0 or not finite),
+ * PKV_ERR_DTYPE, PKV_ERR_ALIGN (q, caches,
  * out must be 16-byte aligned and every stride a multiple of 16 bytes),
  * PKV_ERR_WORKSPACE, PKV_ERR_HIP.  Nothing is launched on error.
  */

@@ -142,7 +142,8 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   if (rc) return rc;
   rc = check_attn_ptrs(q, k_cache, v_cache, block_table, seqlens_k, cu_seqlens_q, out, lse, *l);
   if (rc) return rc;
-  if (!std::isfinite(softmax_scale)) return fail(PKV_ERR_SHAPE, "softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(PKV_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (l->batch == 0 || l->total_q == 0) return ok();
   const Plan p = make_plan(*l);
   bool allocated = false;

@@ -495,6 +495,10 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
 
+  // Consecutive work groups take consecutive chunks of one (sequence, KV
+  // head): concurrently running waves then read different cache blocks
+  // (ordering the KV heads of one chunk next to each other measured ~9%
+  // slower on the long-context workload).
   const int b = blockIdx.z;
   const int hk = blockIdx.y;
   const int cb = blockIdx.x % a.ncb;
@@ -570,13 +574,7 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   }
 }
 
-#ifndef PKV_MERGE_WPR_EXP
-#define PKV_MERGE_WPR_EXP 2
-#endif
-#ifndef PKV_MERGE_PF_EXP
-#define PKV_MERGE_PF_EXP 16
-#endif
-constexpr int kMergeWavesPerRow = PKV_MERGE_WPR_EXP;
+constexpr int kMergeWavesPerRow = 2;
 
 // Fold of one row's chunk partials, ascending chunk index, then the final
 // write.  WPR waves per (row, query head), each owning D / WPR head-dim
@@ -586,7 +584,7 @@ template <class T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int WPR = kMergeWavesPerRow;
   constexpr int EPL = D / 64 / WPR > 0 ? D / 64 / WPR : 1;
-  constexpr int PF = PKV_MERGE_PF_EXP;
+  constexpr int PF = 16;
   const int64_t wg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t w = wg / WPR;
   const int part = static_cast<int>(wg % WPR);

@@ -54,6 +54,11 @@ template <class T> __device__ __forceinline__ float pkv_exp(float x);
 template <> __device__ __forceinline__ float pkv_exp<TBf16>(float x) { return __builtin_amdgcn_exp2f(x); }
 template <> __device__ __forceinline__ float pkv_exp<TF32>(float x) { return expf(x); }
 
+// How far a column's tile max may exceed its reference max before the
+// reference moves (and o, l are rescaled): 8 score units, so p <= 2^8 (bf16,
+// base 2) or e^8 (fp32) -- far from fp32 overflow, and most tiles keep alpha = 1.
+template <class T> constexpr float kRescaleSlack = 8.0f;
+
 // Natural-log LSE from the running max m and sum l (m in the score units of T).
 template <class T> __device__ __forceinline__ float pkv_lse(float m, float l);
 template <> __device__ __forceinline__ float pkv_lse<TBf16>(float m, float l) {
@@ -209,17 +214,22 @@ __device__ __forceinline__ u32x4 v_operand_bf16(const unsigned char* v_lds, int 
 //            that do not exist carry lim = INT_MAX (their values are never
 //            stored)
 //   j0       global position of the tile's first key
-//   mul      score multiplier (scale, times log2(e) for bf16)
-// Steps per column: x = s * mul, masked to -inf for invisible keys; tile max
-// (exact); new running max m_new; alpha = exp(m_old - m_new) (0 when nothing
-// was visible yet); p = exp(x - m_new) (exactly 0 for invisible keys); l =
-// fma(l, alpha, sum of this lane's fp32 p in (mt, i) order); o = o * alpha;
-// o += P V by MFMA in PV-step order, where the bf16 path feeds P to the MFMA
-// rounded once to bf16 (v_cvt_pk_bf16_f32, round to nearest even).  The row
-// sum uses the unrounded p: summing the rounded values would bias the LSE of
-// short rows by up to 2^-9.
-// One shortcut (kShortcuts) changes no bit: when every column of the wave sees
-// the whole tile, the per-key mask is skipped (it would select nothing).
+//   mul      score multiplier, > 0 (scale, times log2(e) for bf16)
+// Steps per column: raw scores of invisible keys set to -inf; tile max of the
+// raw scores (exact) times mul gives the tile max m_tile of the scaled scores.
+// The column keeps a reference max m (-inf before its first visible key); it
+// moves to m_tile only when m is -inf or m_tile > m + slack, with alpha =
+// exp(m_old - m_new) (0 from -inf), else alpha = 1 exactly.  p = exp(s*mul -
+// m) with the product fused (exactly 0 for invisible keys, at most
+// exp(slack)); l = fma(l, alpha, sum of this lane's fp32 p in (mt, i) order);
+// o = o * alpha; o += P V by MFMA in PV-step order, where the bf16 path feeds
+// P to the MFMA rounded once to bf16 (v_cvt_pk_bf16_f32, round to nearest
+// even).  The row sum uses the unrounded p: summing the rounded values would
+// bias the LSE of short rows by up to 2^-9.  Every decision is per column, so
+// a column's bits never depend on the other columns sharing its wave.
+// Two shortcuts change no bit: when every column of the wave sees the whole
+// tile the per-key mask is skipped (kShortcuts; it would select nothing), and
+// when every column's alpha is exactly 1 the multiply of o is skipped.
 // ---------------------------------------------------------------------------
 template <class T, int D, int NT, bool kPinVReads = false, bool kShortcuts = true>
 __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
@@ -234,11 +244,6 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const bool whole = kShortcuts && __all(j0 + KT <= lim[nt]);
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < G_::MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[nt][mt][i] = s[nt][mt][i] * mul;
     if (!whole) {
 #pragma unroll
       for (int mt = 0; mt < G_::MT; ++mt)
@@ -248,32 +253,41 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
           if (key >= lim[nt]) s[nt][mt][i] = -INFINITY;
         }
     }
+    float tmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[nt][mt][i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // mul > 0, so the max of the scaled scores is the scaled max (rounding is monotone).
+    const float m_tile = tmax * mul;
     const float m_old = st.m[nt];
-    const float m_new = fmaxf(m_old, tmax);
-    const float alpha = (m_old == -INFINITY) ? 0.f : pkv_exp<T>(m_old - m_new);
+    float m_new = m_old;
+    float alpha = 1.f;
+    if (m_old == -INFINITY || m_tile > m_old + kRescaleSlack<T>) {
+      m_new = m_tile;
+      alpha = (m_old == -INFINITY) ? 0.f : pkv_exp<T>(m_old - m_new);
+    }
     // Invisible keys hold -inf, so exp gives exactly 0 once the column has a
-    // finite max; a column with nothing visible yet subtracts 0 instead of
-    // -inf (its p are all exp(-inf) = 0).
+    // finite reference; a column with nothing visible yet subtracts 0 instead
+    // of -inf (its p are all exp(-inf) = 0).
     const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
     float tsum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = pkv_exp<T>(s[nt][mt][i] - m_ref);
+        const float p = pkv_exp<T>(fmaf(s[nt][mt][i], mul, -m_ref));
         s[nt][mt][i] = p;
         tsum = tsum + p;
       }
     st.l[nt] = fmaf(st.l[nt], alpha, tsum);
     st.m[nt] = m_new;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int dt = 0; dt < G_::DT; ++dt) st.o[nt][dt] = st.o[nt][dt] * alpha;
+      for (int dt = 0; dt < G_::DT; ++dt) st.o[nt][dt] = st.o[nt][dt] * alpha;
+    }
     if constexpr (T::EB == 2) {
 #pragma unroll
       for (int ks = 0; ks < KT / 32; ++ks) {
