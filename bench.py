@@ -101,6 +101,27 @@ def main():
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
 
+    # the same step as one fused launch (append + attend), timed the same way
+    def fused_step():
+        ev0.record(stream)
+        pkv.attn_forward_append(q, kn, vn, pool.k, pool.v, bt, seqlens, cu, True, scale, max_seqlen_q=1,
+                                max_seqlen_k=N, out=out_f, lse=lse_f, workspace=ws)
+        ev1.record(stream)
+
+    out_f = torch.empty_like(q)
+    lse_f = torch.empty_like(lse)
+    for _ in range(args.warmup):
+        fused_step()
+    torch.cuda.synchronize()
+    fused_ms = 0.0
+    for _ in range(args.steps):
+        fused_step()
+        ev1.synchronize()
+        fused_ms += ev0.elapsed_time(ev1)
+    fused_ms /= args.steps
+    fused_same = bool(torch.equal(out_f.view(torch.int16), out.view(torch.int16))
+                      and torch.equal(lse_f.view(torch.int32), lse.view(torch.int32)))
+
     # bitwise: the prefill kernel on the same rows gives the same bits
     with pkv.options(path=2):
         p_out, p_lse = pkv.attn_forward(q, pool.k, pool.v, bt, seqlens, cu, True, scale, max_seqlen_q=1,
@@ -140,6 +161,9 @@ def main():
         },
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "bitwise_decode_eq_prefill_kernel": bitwise,
+        "fused_append_step": {"api": "pkv_attn_forward_append", "avg_ms": round(fused_ms, 4),
+                              "kv_GBs": round(kv_bytes / (fused_ms * 1e-3) / 1e9, 2),
+                              "bitwise_eq_unfused": fused_same},
     }
     del ws, p_out, p_lse
 

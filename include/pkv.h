@@ -152,6 +152,28 @@ int pkv_attn_forward_ws(const void* q, const void* k_cache, const void* v_cache,
                         float softmax_scale, void* out, float* lse, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Fused append-then-attend: the K/V rows of this call's own query rows are
+ * written into the cache and attended in the same launch.  The step before the
+ * path on the pages (aiter commit d293d61bbf19: flash_attn_with_kvcache
+ * parametrised over new_kv; RL-Kernel issue #152, section Scope: cache writes
+ * must add no precision difference).
+ *   k_new, v_new  device, [total_q, Hkv, d] of dtype: row cu_seqlens_q[b] + r is the
+ *                 key/value of key position seqlens_k[b] - L_b + r (the row's own position)
+ *   k_cache, v_cache  written at those positions (and read as in pkv_attn_forward)
+ *   seqlens_k     keys visible to the call, the appended ones included (as in
+ *                 pkv_attn_forward); requires L_b <= seqlens_k[b]
+ *   workspace     NULL: taken from the stream-ordered allocator; else a caller buffer of
+ *                 workspace_bytes >= pkv_attn_workspace_size(kv_strides)
+ * Result, bit for bit: the cache bytes and out/lse of pkv_cache_write(k_new, v_new,
+ * ..., seqlens_k - L, cu_seqlens_q) followed by pkv_attn_forward(...).  Other
+ * arguments, ownership and errors as pkv_attn_forward.
+ */
+int pkv_attn_forward_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const pkv_layout* kv_strides, const int32_t* block_table, const int32_t* seqlens_k,
+                            const int32_t* cu_seqlens_q, int causal, float softmax_scale, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes the split path needs for this layout (0 if it is never used). */
 size_t pkv_attn_workspace_size(const pkv_layout* kv_strides);
 

@@ -32,6 +32,7 @@ TILE_KEYS = 64
 EXPORTS = (
     "pkv_attn_forward",
     "pkv_attn_forward_ws",
+    "pkv_attn_forward_append",
     "pkv_attn_workspace_size",
     "pkv_cache_write",
     "pkv_validate_layout",
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_attn_forward.restype = i32
     L.pkv_attn_forward_ws.argtypes = [vp, vp, vp, lay, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.pkv_attn_forward_ws.restype = i32
+    L.pkv_attn_forward_append.argtypes = [vp, vp, vp, vp, vp, lay, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.pkv_attn_forward_append.restype = i32
     L.pkv_attn_workspace_size.argtypes = [lay]
     L.pkv_attn_workspace_size.restype = sz
     L.pkv_cache_write.argtypes = [vp, vp, vp, vp, lay, vp, vp, vp, i64, vp]
@@ -204,6 +207,39 @@ def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         rc = L.pkv_attn_forward_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    _stream_handle(q.device))
     _check(rc, "pkv_attn_forward")
+    return out, lse
+
+
+def attn_forward_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, block_table: torch.Tensor, seqlens_k: torch.Tensor,
+                        cu_seqlens_q: torch.Tensor, causal: bool, softmax_scale: float, *, max_seqlen_q: int,
+                        max_seqlen_k: int = 0, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Write ``k_new``/``v_new`` (one row per query row, at the row's own key
+    position ``seqlens_k[b] - L + r``) into the cache and attend, in one launch.
+
+    Bitwise the same cache and ``(out, lse)`` as ``cache_write`` (at
+    ``seqlens_k - L``) followed by ``attn_forward``.
+    """
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [total_q, Hq, d] tensor")
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if t.dim() != 3 or not t.is_contiguous() or t.dtype != k_cache.dtype or t.shape[0] != q.shape[0]:
+            raise ValueError(f"{name} must be a contiguous [total_q, Hkv, d] tensor of the cache dtype")
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().pkv_attn_forward_append(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(lay),
+        _int32(block_table, "block_table").data_ptr(), _int32(seqlens_k, "seqlens_k").data_ptr(),
+        _int32(cu_seqlens_q, "cu_seqlens_q").data_ptr(), 1 if causal else 0, float(softmax_scale), out.data_ptr(),
+        lse.data_ptr(), ws_ptr, ws_bytes, _stream_handle(q.device))
+    _check(rc, "pkv_attn_forward_append")
     return out, lse
 
 

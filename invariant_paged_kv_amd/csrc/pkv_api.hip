@@ -137,15 +137,21 @@ int check_attn_ptrs(const void* q, const void* k, const void* v, const int32_t* 
 int run_attention(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* l,
                   const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
                   float softmax_scale, void* out, float* lse, void* ws, size_t ws_bytes, bool own_ws,
-                  hipStream_t stream) {
+                  hipStream_t stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                  void* k_store = nullptr, void* v_store = nullptr) {
   int rc = validate(l);
   if (rc) return rc;
   rc = check_attn_ptrs(q, k_cache, v_cache, block_table, seqlens_k, cu_seqlens_q, out, lse, *l);
   if (rc) return rc;
+  const bool append = k_store != nullptr;
+  if (append && l->total_q > 0 && (!k_new || !v_new)) return fail(PKV_ERR_NULL, "k_new or v_new is NULL");
+  if (append && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(PKV_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(PKV_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (l->batch == 0 || l->total_q == 0) return ok();
-  const Plan p = make_plan(*l);
+  Plan p = make_plan(*l);
+  p.lp.append = append;
   bool allocated = false;
   if (p.ws_bytes > 0) {
     if (own_ws) {
@@ -184,6 +190,10 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.mul = l->dtype == PKV_BF16 ? static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634074)
                                : softmax_scale;
   pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_store = k_store;
+  a.v_store = v_store;
   hipError_t e = pkv::launch_attention(a, p.lp, l->dtype, l->head_dim, stream);
   if (allocated) {
     hipError_t fe = hipFreeAsync(ws, stream);
@@ -217,6 +227,16 @@ int pkv_attn_forward_ws(const void* q, const void* k_cache, const void* v_cache,
                         hipStream_t stream) {
   return run_attention(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, causal, softmax_scale,
                        out, lse, workspace, workspace_bytes, false, stream);
+}
+
+int pkv_attn_forward_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const pkv_layout* kv_strides, const int32_t* block_table, const int32_t* seqlens_k,
+                            const int32_t* cu_seqlens_q, int causal, float softmax_scale, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!k_cache || !v_cache) return fail(PKV_ERR_NULL, "k_cache or v_cache is NULL");
+  return run_attention(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, causal, softmax_scale,
+                       out, lse, workspace, workspace_bytes, workspace == nullptr, stream, k_new, v_new, k_cache,
+                       v_cache);
 }
 
 int pkv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const pkv_layout* l,

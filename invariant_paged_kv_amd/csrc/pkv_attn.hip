@@ -21,13 +21,60 @@
 
 namespace pkv {
 
+// Fused append: key positions >= n_old are this call's own rows and are read
+// from k_new / v_new (row row0 + position - n_old); the work group with
+// writer set also stores them into the cache, so after the call the cache
+// holds exactly what pkv_cache_write would have put there, and every read saw
+// the same bits it would have read after that write.
+struct Append {
+  int n_old = INT_MAX;  // first appended key position (INT_MAX: no append)
+  int64_t row0 = 0;     // k_new row holding position n_old
+  bool writer = false;  // this work group stores the appended rows
+};
+
+template <bool APPEND>
+__device__ __forceinline__ Append make_append(int n, int L, int q0, bool last_block) {
+  Append ap;
+  if constexpr (APPEND) {
+    ap.n_old = n - L;
+    ap.row0 = q0;
+    ap.writer = last_block;
+  }
+  return ap;
+}
+
+// Address of the 16-byte piece `byte_off` of key row jc (cache address
+// `cache`), redirected to the caller's new rows under fused append.
+template <class T, int D, bool APPEND>
+__device__ __forceinline__ const unsigned char* kv_src(const void* new_base, int nhk, int hk, int jc,
+                                                        const Append& ap, const unsigned char* cache, int byte_off) {
+  if constexpr (APPEND) {
+    const int64_t nrow = (ap.row0 + (jc - ap.n_old)) * nhk + hk;
+    const unsigned char* np = static_cast<const unsigned char*>(new_base) + nrow * D * T::EB + byte_off;
+    return jc >= ap.n_old ? np : cache;
+  } else {
+    return cache;
+  }
+}
+
+template <class T, bool APPEND>
+__device__ __forceinline__ void kv_store_new(const Append& ap, bool in, int jc, void* store_base, const void* load_base,
+                                             const unsigned char* cache, u32x4 x) {
+  if constexpr (APPEND) {
+    if (ap.writer && in && jc >= ap.n_old) {
+      unsigned char* dst = static_cast<unsigned char*>(store_base) + (cache - static_cast<const unsigned char*>(load_base));
+      *reinterpret_cast<u32x4*>(dst) = x;
+    }
+  }
+}
+
 // K/V tile loader: keys j0 .. j0+KT-1 of one sequence and KV head into LDS,
 // 16-byte loads, consecutive lanes on consecutive 16 bytes of a key row.  The
 // block address uses the real block stride (contiguous or K/V-interleaved
 // caches alike).  Keys >= jmax are not read; their rows are zero.
-template <class T, int D, int W>
+template <class T, int D, int W, bool APPEND>
 __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
-                                          unsigned char* k_lds, unsigned char* v_lds) {
+                                          unsigned char* k_lds, unsigned char* v_lds, const Append& ap) {
   using G_ = TileGeom<T, D>;
   constexpr int NCH = KT * G_::CPR;
   constexpr int PER = NCH / (64 * W);
@@ -47,9 +94,14 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
       const int bi = div_block(jc, a.bs_mul, a.bs_shift);
       const int64_t blk = bt[bi];
       const int64_t slot = jc - bi * a.bs;
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::EB + 16 * part);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::EB + 16 * part);
+      const unsigned char* kc = kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::EB + 16 * part;
+      const unsigned char* vc = vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::EB + 16 * part;
+      const int nhk = a.hq / a.g;
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, 16 * part));
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, 16 * part));
       const bool in = j < jmax;
+      kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kc, kv);
+      kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vc, vv);
       kr[i] = in ? kv : u32x4{0, 0, 0, 0};
       vr[i] = in ? vv : u32x4{0, 0, 0, 0};
     }
@@ -89,7 +141,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
   }
 }
 
-template <class T, int D, int W, int NT, bool SPLIT>
+template <class T, int D, int W, int NT, bool SPLIT, bool APPEND>
 __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   constexpr int COLS = W * NT * 16;
@@ -124,6 +176,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
     if (c_begin >= c_end) return;
   }
 
+  const Append ap = make_append<APPEND>(n, L, q0, col0 + COLS >= ncols);
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int G = lane >> 4;
@@ -165,7 +218,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
     const int jend = min((c + 1) * KC, jmax);
     for (int j0 = c * KC; j0 < jend; j0 += KT) {
       __syncthreads();
-      load_tile<T, D, W>(a, bt, hk, j0, jmax, k_lds, v_lds);
+      load_tile<T, D, W, APPEND>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
       __syncthreads();
       f32x4 s[NT][KT / 16];
       KOps<T, D> kop;
@@ -246,9 +299,9 @@ __device__ __forceinline__ void tile_block_ids(const AttnArgs& a, const int32_t*
   }
 }
 
-template <class T, int D>
+template <class T, int D, bool APPEND>
 __device__ __forceinline__ void tile_load_regs(const AttnArgs& a, int hk, int j0, int jlast, const int (&ids)[KT / 16],
-                                               TileRegs<T, D>& r, bool want_k, bool want_v) {
+                                               TileRegs<T, D>& r, bool want_k, bool want_v, const Append& ap) {
   using G_ = TileGeom<T, D>;
   const int lane = lane_id();
   const unsigned char* kb = static_cast<const unsigned char*>(a.k);
@@ -262,14 +315,19 @@ __device__ __forceinline__ void tile_load_regs(const AttnArgs& a, int hk, int j0
     const int64_t slot = jc - div_block(jc, a.bs_mul, a.bs_shift) * a.bs;
     const unsigned char* kp = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::EB + 16 * (lane >> 4);
     const unsigned char* vp = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::EB + 16 * (lane >> 4);
+    const int nhk = a.hq / a.g;
+    const unsigned char* ks = kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kp, 16 * (lane >> 4));
+    const unsigned char* vs = kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vp, 16 * (lane >> 4));
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) {
       if (want_k) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(kp + 64 * k);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(ks + 64 * k);
+        kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kp + 64 * k, x);
         r.k[mt][k] = in ? x : u32x4{0, 0, 0, 0};
       }
       if (want_v) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vp + 64 * k);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(vs + 64 * k);
+        kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vp + 64 * k, x);
         r.v[mt][k] = in ? x : u32x4{0, 0, 0, 0};
       }
     }
@@ -307,9 +365,9 @@ struct PrefillStage {
   u32x4 v[PER];
 };
 
-template <class T, int D, int W>
+template <class T, int D, int W, bool APPEND>
 __device__ __forceinline__ void prefill_load(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
-                                             PrefillStage<T, D, W>& r) {
+                                             PrefillStage<T, D, W>& r, const Append& ap) {
   using G_ = TileGeom<T, D>;
   using S_ = PrefillStage<T, D, W>;
   static_assert(S_::PER * 64 * W == S_::NCH, "tile pieces must split evenly over the work group");
@@ -324,9 +382,14 @@ __device__ __forceinline__ void prefill_load(const AttnArgs& a, const int32_t* b
     const int bi = div_block(jc, a.bs_mul, a.bs_shift);
     const int64_t blk = bt[bi];
     const int64_t slot = jc - bi * a.bs;
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::EB + 16 * part);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::EB + 16 * part);
+    const unsigned char* kc = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::EB + 16 * part;
+    const unsigned char* vc = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::EB + 16 * part;
+    const int nhk = a.hq / a.g;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, 16 * part));
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, 16 * part));
     const bool in = j < jmax;
+    kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kc, kv);
+    kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vc, vv);
     r.k[i] = in ? kv : u32x4{0, 0, 0, 0};
     r.v[i] = in ? vv : u32x4{0, 0, 0, 0};
   }
@@ -374,14 +437,15 @@ __device__ __forceinline__ void qk_tile_lds(const unsigned char* k_lds, const QO
 
 // One prefill tile: `cur` is refilled with tile t+2 while tile t is computed
 // from LDS buffer t&1; `nxt` (tile t+1) goes to LDS buffer (t+1)&1 afterwards.
-template <class T, int D, int W>
+template <class T, int D, int W, bool APPEND>
 __device__ __forceinline__ void prefill_tile(const AttnArgs& a, const int32_t* bt, int hk, int t, int ntiles, int jmax,
                                              unsigned char* lds, PrefillStage<T, D, W>& cur,
                                              PrefillStage<T, D, W>& nxt, const QOps<T, D>& q, const int (&lim)[1],
-                                             ChunkState<D, 1>& st, float& M, float& Ls, f32x4 (&O)[D / 16]) {
+                                             ChunkState<D, 1>& st, float& M, float& Ls, f32x4 (&O)[D / 16],
+                                             const Append& ap) {
   using G_ = TileGeom<T, D>;
   const int j0 = t * KT;
-  if (t + 2 < ntiles) prefill_load<T, D, W>(a, bt, hk, j0 + 2 * KT, jmax, cur);
+  if (t + 2 < ntiles) prefill_load<T, D, W, APPEND>(a, bt, hk, j0 + 2 * KT, jmax, cur, ap);
   const unsigned char* k_lds = lds + (t & 1) * G_::BYTES;
   f32x4 s[1][KT / 16];
   qk_tile_lds<T, D>(k_lds, q, s[0]);
@@ -407,7 +471,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, const int32_t* b
   __syncthreads();
 }
 
-template <class T, int D, int W>
+template <class T, int D, int W, bool APPEND>
 __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   constexpr int COLS = W * 16;
@@ -439,6 +503,7 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
   const int last_col = min(col0 + COLS, ncols) - 1;
   const int jmax = column_limit(last_col, ncols, g, n, L, a.causal);
   const int ntiles = jmax > 0 ? (jmax + KT - 1) / KT : 0;
+  const Append ap = make_append<APPEND>(n, L, q0, col0 + COLS >= ncols);
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -466,8 +531,8 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
   // t+1 (loaded during tile t-1) and the other receives tile t+2.
   PrefillStage<T, D, W> sa, sb;
   if (ntiles > 0) {
-    prefill_load<T, D, W>(a, bt, hk, 0, jmax, sa);
-    if (ntiles > 1) prefill_load<T, D, W>(a, bt, hk, KT, jmax, sb);
+    prefill_load<T, D, W, APPEND>(a, bt, hk, 0, jmax, sa, ap);
+    if (ntiles > 1) prefill_load<T, D, W, APPEND>(a, bt, hk, KT, jmax, sb, ap);
     prefill_store<T, D, W>(lds, lds + G_::KBYTES, sa);
   }
   __syncthreads();
@@ -475,9 +540,9 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
   chunk_reset(st);
   for (int t = 0; t < ntiles; ++t) {
     if ((t & 1) == 0) {
-      prefill_tile<T, D, W>(a, bt, hk, t, ntiles, jmax, lds, sa, sb, q, lim, st, M, Ls, O);
+      prefill_tile<T, D, W, APPEND>(a, bt, hk, t, ntiles, jmax, lds, sa, sb, q, lim, st, M, Ls, O, ap);
     } else {
-      prefill_tile<T, D, W>(a, bt, hk, t, ntiles, jmax, lds, sb, sa, q, lim, st, M, Ls, O);
+      prefill_tile<T, D, W, APPEND>(a, bt, hk, t, ntiles, jmax, lds, sb, sa, q, lim, st, M, Ls, O, ap);
     }
   }
 
@@ -490,7 +555,7 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
 
 // Two waves per SIMD (<= 256 registers): 8 waves per CU, each with one tile
 // (32 KiB at d = 128) of K/V loads in flight while it computes the previous one.
-template <class T, int D>
+template <class T, int D, bool APPEND>
 __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
@@ -517,6 +582,7 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   const int c_end = min(min(c_begin + a.cpi, nchunks), a.maxc);
   if (c_begin >= c_end) return;
   const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
+  const Append ap = make_append<APPEND>(n, L, q0, col0 + 16 >= ncols);
 
   const int lane = lane_id();
   const int G = lane >> 4;
@@ -538,7 +604,7 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   int ids[KT / 16];
   TileRegs<T, D> r;
   tile_block_ids(a, bt, j0, jlast, ids);
-  tile_load_regs<T, D>(a, hk, j0, jlast, ids, r, true, true);
+  tile_load_regs<T, D, APPEND>(a, hk, j0, jlast, ids, r, true, true, ap);
   tile_block_ids(a, bt, j0 + KT, jlast, ids);
 
   // Per tile: copy V(t) to LDS and refill those registers with V(t+1); QK on
@@ -551,11 +617,11 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
       const int jn = j0 + KT;
       const bool more = jn < jlast;
       tile_store_v<T, D>(v_lds, r);
-      if (more) tile_load_regs<T, D>(a, hk, jn, jlast, ids, r, false, true);
+      if (more) tile_load_regs<T, D, APPEND>(a, hk, jn, jlast, ids, r, false, true, ap);
       f32x4 s[1][KT / 16];
       qk_tile<T, D>(r.k, q, s[0]);
       if (more) {
-        tile_load_regs<T, D>(a, hk, jn, jlast, ids, r, true, false);
+        tile_load_regs<T, D, APPEND>(a, hk, jn, jlast, ids, r, true, false, ap);
         tile_block_ids(a, bt, jn + KT, jlast, ids);
       }
       softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
@@ -647,26 +713,26 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 // ---------------------------------------------------------------------------
 // Host-side launchers (called by pkv_api.hip after validation).
 // ---------------------------------------------------------------------------
-template <class T, int D>
+template <class T, int D, bool APPEND>
 static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStream_t stream) {
   if (pl.full) {
     dim3 grid(a.ncb, pl.hk, pl.batch);
     if constexpr (T::EB == 2) {
-      hipLaunchKernelGGL((prefill_kernel<T, D, 8>), grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((prefill_kernel<T, D, 8, APPEND>), grid, dim3(512), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false, APPEND>), grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();
   }
   dim3 grid(a.ncb * pl.items, pl.hk, pl.batch);
   if (pl.waves == 1) {
     if constexpr (T::EB == 2) {
-      hipLaunchKernelGGL((decode_kernel<T, D>), grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((decode_kernel<T, D, APPEND>), grid, dim3(64), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true>), grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true, APPEND>), grid, dim3(64), 0, stream, a);
     }
   } else {
-    hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, true, APPEND>), grid, dim3(256), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -689,12 +755,17 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   return hipGetLastError();
 }
 
+template <bool APPEND>
+static hipError_t launch_attention_t(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream) {
+  if (dtype == 1) {
+    return d == 128 ? launch_attn_t<TBf16, 128, APPEND>(a, pl, stream) : launch_attn_t<TBf16, 64, APPEND>(a, pl, stream);
+  }
+  return d == 128 ? launch_attn_t<TF32, 128, APPEND>(a, pl, stream) : launch_attn_t<TF32, 64, APPEND>(a, pl, stream);
+}
+
 hipError_t launch_attention(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream) {
   (void)hipGetLastError();
-  if (dtype == 1) {
-    return d == 128 ? launch_attn_t<TBf16, 128>(a, pl, stream) : launch_attn_t<TBf16, 64>(a, pl, stream);
-  }
-  return d == 128 ? launch_attn_t<TF32, 128>(a, pl, stream) : launch_attn_t<TF32, 64>(a, pl, stream);
+  return pl.append ? launch_attention_t<true>(a, pl, dtype, d, stream) : launch_attention_t<false>(a, pl, dtype, d, stream);
 }
 
 }  // namespace pkv

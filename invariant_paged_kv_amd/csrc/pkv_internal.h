@@ -28,6 +28,14 @@ struct AttnArgs {
   float mul;       // score multiplier: scale (fp32) or scale*log2(e) (bf16)
   uint32_t bs_mul; // j / bs == (j * bs_mul) >> bs_shift for 0 <= j < 2^30
   int32_t bs_shift;
+  // Fused append (pkv_attn_forward_append): the K/V rows of this call's query
+  // rows, [total_q, Hkv, d]; row r of sequence b holds key position
+  // seqlens_k[b] - L_b + r.  Reads of those positions take them from here and
+  // one work group per (sequence, KV head) stores them into the cache.
+  const void* k_new;
+  const void* v_new;
+  void* k_store;
+  void* v_store;
 };
 
 struct MergeArgs {
@@ -43,6 +51,7 @@ struct MergeArgs {
 
 struct LaunchPlan {
   bool full;       // prefill kernel (true) or split kernels + merge (false)
+  bool append;     // fused append of k_new / v_new
   int waves;       // split path: waves per work group (1 or 4)
   int items;       // split path: work items per column block along the keys
   int batch, hk;
