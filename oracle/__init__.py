@@ -1,4 +1,4 @@
-"""CPU oracle for the paged-KV attention forward.
+"""CPU oracle for the paged-KV attention forward and backward.
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import, call or run anything in this
@@ -14,7 +14,9 @@ result is.
 Pins (see ``tests/test_oracle.py``): every function here is checked against
 something other than itself -- a pure-Python ``decimal`` brute force over a
 nested-list pool, PyTorch's own float64 scaled-dot-product attention, closed
-forms, and the invariances the pages state.  No function in this package is
+forms, and the invariances the pages state; the backward against PyTorch's
+float64 autograd, central finite differences of the forward, and the
+gradient identities of softmax (``tests/test_oracle_backward.py``).  No function in this package is
 "parity unpinned".
 """
 
@@ -28,4 +30,9 @@ from .paged_kv import (  # noqa: F401
     scores,
     row_positions,
     visible_keys,
+)
+from .backward import (  # noqa: F401
+    attention_backward,
+    attention_backward_bound,
+    cu_seqlens_k_of,
 )

@@ -57,7 +57,7 @@ class Layout:
     = block_size*nheads_k*d`` and the block stride is ``2*block_size*nheads_k*d``.
     """
 
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32" or "bf16" ("f64" for exact float64 inputs)
     num_heads_q: int
     num_heads_k: int
     head_dim: int
@@ -83,6 +83,8 @@ def _as_f64(values: np.ndarray, dtype: str) -> np.ndarray:
         return bf16_bits_to_f64(values)
     if dtype == "f32":
         return np.asarray(values, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":  # exact float64 inputs (finite-difference checks)
+        return np.asarray(values, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

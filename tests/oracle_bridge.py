@@ -56,3 +56,21 @@ def oracle_attention(q: torch.Tensor, pool: PagedKV, block_table, seqlens_k,
                             [int(x) for x in torch.as_tensor(seqlens_k).cpu()],
                             [int(x) for x in torch.as_tensor(cu_seqlens_q).cpu()],
                             causal, softmax_scale)
+
+
+def oracle_backward(q: torch.Tensor, pool: PagedKV, block_table, seqlens_k,
+                    cu_seqlens_q, causal: bool, softmax_scale: float,
+                    dout: torch.Tensor, bound: bool = False):
+    """Run the backward oracle on generator tensors; float64 ``(dq, dk, dv)``.
+
+    With ``bound=True`` the term-magnitude bounds ``(Aq, Ak, Av)`` come back
+    instead (used to scale the GPU tolerances).
+    """
+    hq = q.shape[1]
+    kf, vf, lay = oracle_pool(pool, hq)
+    fn = oracle.attention_backward_bound if bound else oracle.attention_backward
+    return fn(storage_np(q).reshape(q.shape), kf, vf, lay,
+              np.asarray(torch.as_tensor(block_table).cpu()),
+              [int(x) for x in torch.as_tensor(seqlens_k).cpu()],
+              [int(x) for x in torch.as_tensor(cu_seqlens_q).cpu()],
+              causal, softmax_scale, storage_np(dout).reshape(dout.shape))
