@@ -178,6 +178,42 @@ int pkv_attn_forward_append(const void* q, const void* k_new, const void* v_new,
 size_t pkv_attn_workspace_size(const pkv_layout* kv_strides);
 
 /*
+ * Backward of pkv_attn_forward: gradients of out with respect to q and to each
+ * sequence's visible keys and values.  RL-Kernel PR #284, "feat(attention):
+ * add CP backward drift validation", sections Summary and Changes: a
+ * deterministic training backward (dq, dk, dv) for causal prefill and chunked
+ * prefill over the same forward, fp32 accumulation, one downcast at the final
+ * write.  The cotangent of lse is taken as zero.
+ *   q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q,
+ *   causal, softmax_scale   exactly as given to the forward
+ *   out, lse        device, the forward's outputs for those inputs
+ *   dout            device, [total_q, Hq, d] of dtype: the cotangent of out
+ *   cu_seqlens_k    device int32 [batch + 1]: exclusive prefix sum of seqlens_k
+ *                   (precondition, not checked on the device)
+ *   total_k         host copy of cu_seqlens_k[batch]
+ *   dq              device, [total_q, Hq, d] of dtype (written, every row)
+ *   dk, dv          device, [total_k, Hkv, d] of dtype: row cu_seqlens_k[b] + j is
+ *                   key/value position j of sequence b; every such row is written
+ *                   (query heads of a GQA group add up)
+ *   workspace       NULL: taken from the stream-ordered allocator; else a caller
+ *                   buffer of workspace_bytes >= pkv_attn_backward_workspace_size()
+ * Every sum runs in an order fixed by global key positions and column indices
+ * (no atomics): results are bitwise reproducible, independent of the batch, and
+ * a row's dq does not depend on how the rows were split into calls.
+ * Errors as pkv_attn_forward; dout, dq, dk, dv, out must be 16-byte aligned.
+ */
+int pkv_attn_backward(const void* q, const void* k_cache, const void* v_cache,
+                      const pkv_layout* kv_strides, const int32_t* block_table,
+                      const int32_t* seqlens_k, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, int64_t total_k, int causal,
+                      float softmax_scale, const void* out, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Workspace bytes pkv_attn_backward needs for this layout (total_q * Hq floats). */
+size_t pkv_attn_backward_workspace_size(const pkv_layout* kv_strides);
+
+/*
  * Append new K/V rows to the paged cache.  RL-Kernel issue #152, section Scope:
  * the write is a bit copy, so the path that wrote the cache and the path that
  * reads it see the same values.

@@ -34,6 +34,8 @@ EXPORTS = (
     "pkv_attn_forward_ws",
     "pkv_attn_forward_append",
     "pkv_attn_workspace_size",
+    "pkv_attn_backward",
+    "pkv_attn_backward_workspace_size",
     "pkv_cache_write",
     "pkv_validate_layout",
     "pkv_set_option",
@@ -95,6 +97,10 @@ def lib() -> ctypes.CDLL:
     L.pkv_attn_forward_append.restype = i32
     L.pkv_attn_workspace_size.argtypes = [lay]
     L.pkv_attn_workspace_size.restype = sz
+    L.pkv_attn_backward.argtypes = [vp, vp, vp, lay, vp, vp, vp, vp, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.pkv_attn_backward.restype = i32
+    L.pkv_attn_backward_workspace_size.argtypes = [lay]
+    L.pkv_attn_backward_workspace_size.restype = sz
     L.pkv_cache_write.argtypes = [vp, vp, vp, vp, lay, vp, vp, vp, i64, vp]
     L.pkv_cache_write.restype = i32
     L.pkv_validate_layout.argtypes = [lay]
@@ -241,6 +247,59 @@ def attn_forward_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
         lse.data_ptr(), ws_ptr, ws_bytes, _stream_handle(q.device))
     _check(rc, "pkv_attn_forward_append")
     return out, lse
+
+
+def attn_backward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                  seqlens_k: torch.Tensor, cu_seqlens_q: torch.Tensor, causal: bool, softmax_scale: float,
+                  out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, *, max_seqlen_q: int,
+                  max_seqlen_k: int = 0, cu_seqlens_k: Optional[torch.Tensor] = None,
+                  total_k: Optional[int] = None, dq: Optional[torch.Tensor] = None,
+                  dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients ``(dq, dk, dv)`` of ``out`` for cotangent ``dout``.
+
+    ``out``/``lse`` are the forward's outputs for the same inputs.  ``dk``/``dv``
+    are ``[total_k, Hkv, d]``: row ``cu_seqlens_k[b] + j`` is key position ``j``
+    of sequence ``b``.  Without ``cu_seqlens_k``/``total_k`` they are computed
+    from ``seqlens_k`` (``total_k`` then needs one device-to-host copy).
+    """
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [total_q, Hq, d] tensor")
+    for t, name in ((out, "out"), (dout, "dout")):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor of q's shape and dtype")
+    if lse.shape != q.shape[:2] or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [total_q, Hq] tensor")
+    sk = _int32(seqlens_k, "seqlens_k")
+    if cu_seqlens_k is None:
+        cu_seqlens_k = torch.zeros(sk.numel() + 1, dtype=torch.int32, device=sk.device)
+        cu_seqlens_k[1:] = torch.cumsum(sk, 0)
+    cuk = _int32(cu_seqlens_k, "cu_seqlens_k")
+    if total_k is None:
+        total_k = int(cuk[-1].item())
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k)
+    hk, d = k_cache.shape[2], k_cache.shape[3]
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty((total_k, hk, d), dtype=q.dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((total_k, hk, d), dtype=q.dtype, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().pkv_attn_backward(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(lay),
+        _int32(block_table, "block_table").data_ptr(), sk.data_ptr(), _int32(cu_seqlens_q, "cu_seqlens_q").data_ptr(),
+        cuk.data_ptr(), int(total_k), 1 if causal else 0, float(softmax_scale), out.data_ptr(), lse.data_ptr(),
+        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes, _stream_handle(q.device))
+    _check(rc, "pkv_attn_backward")
+    return dq, dk, dv
+
+
+def backward_workspace_size(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_table: torch.Tensor, max_seqlen_q: int) -> int:
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], 0)
+    return int(lib().pkv_attn_backward_workspace_size(ctypes.byref(lay)))
 
 
 def workspace_size(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

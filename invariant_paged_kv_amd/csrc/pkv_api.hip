@@ -203,6 +203,86 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   return ok();
 }
 
+size_t backward_ws_bytes(const pkv_layout& l) {
+  return round256(static_cast<size_t>(l.total_q) * l.num_heads_q * sizeof(float));
+}
+
+int run_backward(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* l,
+                 const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q,
+                 const int32_t* cu_seqlens_k, int64_t total_k, int causal, float softmax_scale, const void* out,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  int rc = validate(l);
+  if (rc) return rc;
+  rc = check_attn_ptrs(q, k_cache, v_cache, block_table, seqlens_k, cu_seqlens_q, out, lse, *l);
+  if (rc) return rc;
+  if (total_k < 0) return fail(PKV_ERR_SHAPE, "total_k %lld < 0", (long long)total_k);
+  if (l->total_q > 0 && (!dout || !dq)) return fail(PKV_ERR_NULL, "dout or dq is NULL");
+  if (total_k > 0 && (!dk || !dv)) return fail(PKV_ERR_NULL, "dk or dv is NULL");
+  if (l->batch > 0 && !cu_seqlens_k) return fail(PKV_ERR_NULL, "cu_seqlens_k is NULL");
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(PKV_ERR_ALIGN, "dout, dq, dk and dv must be 16-byte aligned");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(PKV_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (l->batch == 0 || (l->total_q == 0 && total_k == 0)) return ok();
+  const size_t need = backward_ws_bytes(*l);
+  bool allocated = false;
+  if (need > 0) {
+    if (!ws) {
+      if (hipMallocAsync(&ws, need, stream) != hipSuccess)
+        return fail(PKV_ERR_WORKSPACE, "hipMallocAsync of %zu workspace bytes failed", need);
+      allocated = true;
+    } else if (ws_bytes < need || !aligned16(ws)) {
+      return fail(PKV_ERR_WORKSPACE, "backward workspace needs %zu bytes, 16-byte aligned (got %zu)", need, ws_bytes);
+    }
+  }
+  constexpr int kWaves = 4;
+  const int g = l->num_heads_q / l->num_heads_k;
+  const int64_t cols = static_cast<int64_t>(l->max_seqlen_q) * g;
+  const int64_t mk = max_seqlen_k_of(*l);
+  pkv::BwdArgs b{};
+  pkv::AttnArgs& a = b.f;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.block_table = block_table;
+  a.seqlens_k = seqlens_k;
+  a.cu_q = cu_seqlens_q;
+  a.kbs = l->k_block_stride;
+  a.kss = l->k_slot_stride;
+  a.khs = l->k_head_stride;
+  a.vbs = l->v_block_stride;
+  a.vss = l->v_slot_stride;
+  a.vhs = l->v_head_stride;
+  a.hq = l->num_heads_q;
+  a.g = g;
+  a.bs = l->block_size;
+  a.mbps = l->max_blocks_per_seq;
+  a.ncb = static_cast<int>((cols + 16 * kWaves - 1) / (16 * kWaves));
+  a.causal = causal ? 1 : 0;
+  a.mul = l->dtype == PKV_BF16 ? static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634074)
+                               : softmax_scale;
+  pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
+  b.cu_k = cu_seqlens_k;
+  b.out = out;
+  b.lse = lse;
+  b.dout = dout;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.delta = static_cast<float*>(ws);
+  b.scale = softmax_scale;
+  b.nkb = total_k > 0 ? static_cast<int>((mk + 16 * kWaves - 1) / (16 * kWaves)) : 0;
+  pkv::BwdPlan pl{l->batch, l->num_heads_k, l->total_q};
+  hipError_t e = pkv::launch_backward(b, pl, l->dtype, l->head_dim, stream);
+  if (allocated) {
+    hipError_t fe = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && fe != hipSuccess) e = fe;
+  }
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,6 +317,20 @@ int pkv_attn_forward_append(const void* q, const void* k_new, const void* v_new,
   return run_attention(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, causal, softmax_scale,
                        out, lse, workspace, workspace_bytes, workspace == nullptr, stream, k_new, v_new, k_cache,
                        v_cache);
+}
+
+int pkv_attn_backward(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* kv_strides,
+                      const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, int64_t total_k, int causal, float softmax_scale, const void* out,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return run_backward(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, cu_seqlens_k, total_k,
+                      causal, softmax_scale, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+size_t pkv_attn_backward_workspace_size(const pkv_layout* kv_strides) {
+  if (validate(kv_strides) != PKV_OK) return 0;
+  return backward_ws_bytes(*kv_strides);
 }
 
 int pkv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const pkv_layout* l,

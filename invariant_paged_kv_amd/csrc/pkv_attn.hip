@@ -18,111 +18,9 @@
 // the split count or the grid.
 #include "pkv_device.hpp"
 #include "pkv_internal.h"
+#include "pkv_tiles.hpp"
 
 namespace pkv {
-
-// Fused append: key positions >= n_old are this call's own rows and are read
-// from k_new / v_new (row row0 + position - n_old); the work group with
-// writer set also stores them into the cache, so after the call the cache
-// holds exactly what pkv_cache_write would have put there, and every read saw
-// the same bits it would have read after that write.
-struct Append {
-  int n_old = INT_MAX;  // first appended key position (INT_MAX: no append)
-  int64_t row0 = 0;     // k_new row holding position n_old
-  bool writer = false;  // this work group stores the appended rows
-};
-
-template <bool APPEND>
-__device__ __forceinline__ Append make_append(int n, int L, int q0, bool last_block) {
-  Append ap;
-  if constexpr (APPEND) {
-    ap.n_old = n - L;
-    ap.row0 = q0;
-    ap.writer = last_block;
-  }
-  return ap;
-}
-
-// Address of the 16-byte piece `byte_off` of key row jc (cache address
-// `cache`), redirected to the caller's new rows under fused append.
-template <class T, int D, bool APPEND>
-__device__ __forceinline__ const unsigned char* kv_src(const void* new_base, int nhk, int hk, int jc,
-                                                        const Append& ap, const unsigned char* cache, int byte_off) {
-  if constexpr (APPEND) {
-    const int64_t nrow = (ap.row0 + (jc - ap.n_old)) * nhk + hk;
-    const unsigned char* np = static_cast<const unsigned char*>(new_base) + nrow * D * T::EB + byte_off;
-    return jc >= ap.n_old ? np : cache;
-  } else {
-    return cache;
-  }
-}
-
-template <class T, bool APPEND>
-__device__ __forceinline__ void kv_store_new(const Append& ap, bool in, int jc, void* store_base, const void* load_base,
-                                             const unsigned char* cache, u32x4 x) {
-  if constexpr (APPEND) {
-    if (ap.writer && in && jc >= ap.n_old) {
-      unsigned char* dst = static_cast<unsigned char*>(store_base) + (cache - static_cast<const unsigned char*>(load_base));
-      *reinterpret_cast<u32x4*>(dst) = x;
-    }
-  }
-}
-
-// K/V tile loader: keys j0 .. j0+KT-1 of one sequence and KV head into LDS,
-// 16-byte loads, consecutive lanes on consecutive 16 bytes of a key row.  The
-// block address uses the real block stride (contiguous or K/V-interleaved
-// caches alike).  Keys >= jmax are not read; their rows are zero.
-template <class T, int D, int W, bool APPEND>
-__device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
-                                          unsigned char* k_lds, unsigned char* v_lds, const Append& ap) {
-  using G_ = TileGeom<T, D>;
-  constexpr int NCH = KT * G_::CPR;
-  constexpr int PER = NCH / (64 * W);
-  static_assert(PER * 64 * W == NCH, "tile chunks must split evenly over the work group");
-  constexpr int R = PER < 16 ? PER : 16;
-  const unsigned char* kb = static_cast<const unsigned char*>(a.k);
-  const unsigned char* vb = static_cast<const unsigned char*>(a.v);
-#pragma unroll
-  for (int r0 = 0; r0 < PER; r0 += R) {
-    u32x4 kr[R], vr[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int qi = threadIdx.x + (r0 + i) * 64 * W;
-      const int row = qi / G_::CPR, part = qi % G_::CPR;
-      const int j = j0 + row;
-      const int jc = min(j, jmax - 1);  // rows past jmax load a visible row, then read as zero
-      const int bi = div_block(jc, a.bs_mul, a.bs_shift);
-      const int64_t blk = bt[bi];
-      const int64_t slot = jc - bi * a.bs;
-      const unsigned char* kc = kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::EB + 16 * part;
-      const unsigned char* vc = vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::EB + 16 * part;
-      const int nhk = a.hq / a.g;
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, 16 * part));
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, 16 * part));
-      const bool in = j < jmax;
-      kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kc, kv);
-      kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vc, vv);
-      kr[i] = in ? kv : u32x4{0, 0, 0, 0};
-      vr[i] = in ? vv : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int qi = threadIdx.x + (r0 + i) * 64 * W;
-      const int row = qi / G_::CPR, part = qi % G_::CPR;
-      *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = kr[i];
-      *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = vr[i];
-    }
-  }
-}
-
-// Keys visible to column `col` of a sequence: j < limit.  Columns are ordered
-// row-major over (row r, head-in-group hh): col = r * g + hh.  Row r sits at
-// key position n - L + r (bottom-right alignment).
-__device__ __forceinline__ int column_limit(int col, int ncols, int g, int n, int L, int causal) {
-  if (col >= ncols) return INT_MAX;  // no such column: its values are never stored
-  const int p = n - L + col / g;
-  return causal ? min(p + 1, n) : n;
-}
 
 template <class T, int D>
 __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (&o)[D / 16], float M, float Ls) {

@@ -1,0 +1,419 @@
+// pkv_attn_bwd.hip -- backward of the paged-KV attention for gfx950.
+//
+// RL-Kernel PR #284, "feat(attention): add CP backward drift validation",
+// sections "Summary" and "Changes": a deterministic training backward (dq, dk,
+// dv) over the same forward, with fp32 accumulation, a fixed summation order
+// and one downcast at the final write.  With P the softmax weights recomputed
+// from the forward's LSE, dO the cotangent of out and delta = <dO, out> per
+// (row, head):
+//
+//   dP = dO V^T,  dS = P (dP - delta),  dQ = scale dS K,
+//   dK = scale dS^T Q (summed over the heads of a GQA group),  dV = P^T dO.
+//
+// Three kernels, no atomics, every sum in an order fixed by global positions:
+//   bwd_delta_kernel  delta per (row, head): 16 lanes, a fixed butterfly.
+//   bwd_dq_kernel     one work group per (sequence, KV head, 16 W columns);
+//                     K/V tiles staged in LDS in ascending key order from
+//                     key 0, so a column's dq is the same sum whichever call,
+//                     batch or grid computes it.
+//   bwd_dkdv_kernel   one work group per (sequence, KV head, 16 W keys); each
+//                     wave holds its 16 keys' K and V as MFMA operands in
+//                     registers and walks the sequence's columns in
+//                     ascending 32-column steps from column 0 (the first
+//                     steps that cannot see its keys are skipped).
+//
+// A "column" is one (query row, query head of the group) pair, col = r g + hh,
+// as in the forward.  bf16 products use v_mfma_f32_16x16x32_bf16 with P and dS
+// rounded once to bf16 (round to nearest even) as MFMA operands; fp32 uses
+// v_mfma_f32_16x16x4_f32.
+#include "pkv_device.hpp"
+#include "pkv_internal.h"
+#include "pkv_tiles.hpp"
+
+namespace pkv {
+
+// Natural-log LSE in the score units of T (bf16 scores are in base 2).
+template <class T> __device__ __forceinline__ float lse_units(float lse);
+template <> __device__ __forceinline__ float lse_units<TBf16>(float lse) { return lse * 1.44269504088896340736f; }
+template <> __device__ __forceinline__ float lse_units<TF32>(float lse) { return lse; }
+
+__device__ __forceinline__ float elem_f32(const void* p, int64_t i, int eb) {
+  if (eb == 2) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  return static_cast<const float*>(p)[i];
+}
+
+// ---------------------------------------------------------------------------
+// delta[w] = <dout[w], out[w]> for each (row, head) w, in fp32: 16 lanes per w,
+// each lane sums D/16 consecutive elements in ascending order, then a fixed
+// xor butterfly over the 16 lanes.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t pairs) {
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  constexpr int EPL = D / 16;
+  float acc = 0.f;
+  if (w < pairs) {
+    const int64_t e0 = w * D + sub * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = fmaf(elem_f32(a.dout, e0 + e, T::EB), elem_f32(a.out, e0 + e, T::EB), acc);
+  }
+  acc = acc + __shfl_xor(acc, 8);
+  acc = acc + __shfl_xor(acc, 4);
+  acc = acc + __shfl_xor(acc, 2);
+  acc = acc + __shfl_xor(acc, 1);
+  if (w < pairs && sub == 0) a.delta[w] = acc;
+}
+
+// A-operand rows of an LDS tile (row pitch `pitch`): rows 16 mt + l%16,
+// bytes [64k + 16G, +16) -- the layout of KOps, for any row-major tile.
+template <class T, int D>
+__device__ __forceinline__ void row_operands_lds(const unsigned char* lds, int pitch, KOps<T, D>& op) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const unsigned char* base = lds + (lane & 15) * pitch + 16 * (lane >> 4);
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) op[mt][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * pitch + 64 * k);
+}
+
+// One 16x16 product over the head dimension: sum over d of A[m][d] B[n][d],
+// both operands in the QK layout (16 bytes per lane per step), ascending
+// steps from a zero accumulator.
+template <class T, int NK>
+__device__ __forceinline__ f32x4 dot_tile(const u32x4 (&x)[NK], const u32x4 (&y)[NK]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    if constexpr (T::EB == 2) {
+      acc = mfma_bf16(x[k], y[k], acc);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma_f32(__uint_as_float(x[k][e]), __uint_as_float(y[k][e]), acc);
+    }
+  }
+  return acc;
+}
+
+// Two fp32 quadruples rounded to bf16 and packed as one 16x16x32 operand:
+// slots 8G + e hold a[e] (e < 4) and b[e - 4] (e >= 4).
+__device__ __forceinline__ u32x4 pack_bf16(const f32x4& a, const f32x4& b) {
+  const bf16x2 p0 = {(__bf16)a[0], (__bf16)a[1]};
+  const bf16x2 p1 = {(__bf16)a[2], (__bf16)a[3]};
+  const bf16x2 p2 = {(__bf16)b[0], (__bf16)b[1]};
+  const bf16x2 p3 = {(__bf16)b[2], (__bf16)b[3]};
+  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
+               __builtin_bit_cast(uint32_t, p3)};
+}
+
+// Final write of a transposed accumulator (lane l: output row l%16, head-dim
+// elements 16 dt + 4G + i), times `mul`, rounded once to the output type.
+template <class T, int D>
+__device__ __forceinline__ void store_grad(void* dst, int64_t elem, const f32x4 (&acc)[D / 16], float mul) {
+  const int G = lane_id() >> 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int e = 16 * dt + 4 * G;
+    const float v0 = acc[dt][0] * mul, v1 = acc[dt][1] * mul, v2 = acc[dt][2] * mul, v3 = acc[dt][3] * mul;
+    if constexpr (T::EB == 2) {
+      u32x2 w = {bf16_rne_bits(v0) | (bf16_rne_bits(v1) << 16), bf16_rne_bits(v2) | (bf16_rne_bits(v3) << 16)};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + elem + e) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + elem + e) = f32x4{v0, v1, v2, v3};
+    }
+  }
+}
+
+// The QK-layout operands (16 bytes per lane per step) of one row of a
+// [rows, Hq, d] tensor: `row_head` = row * Hq + head.
+template <class T, int D>
+__device__ __forceinline__ void row_operands_global(const void* base, int64_t row_head, bool exists, QOps<T, D>& op) {
+  using G_ = TileGeom<T, D>;
+  const unsigned char* p = static_cast<const unsigned char*>(base) + row_head * D * T::EB + 16 * (lane_id() >> 4);
+#pragma unroll
+  for (int k = 0; k < G_::NK; ++k) op.v[k] = exists ? *reinterpret_cast<const u32x4*>(p + 64 * k) : u32x4{0, 0, 0, 0};
+}
+
+// ---------------------------------------------------------------------------
+// dq: per column, over key tiles 0, 64, 128, ... up to its last visible key:
+//   S^T = K Q^T, dP^T = V dO^T (keys as M, columns as N, as the forward's QK),
+//   P = exp(S * mul - lse), dS = P (dP - delta) (0 for invisible keys),
+//   dQ^T += K^T dS^T (head dim as M, keys as the k-dimension, as the forward's PV).
+// ---------------------------------------------------------------------------
+template <class T, int D, int W>
+__global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
+  const AttnArgs& a = ba.f;
+  using G_ = TileGeom<T, D>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[G_::BYTES];
+  unsigned char* k_lds = lds;
+  unsigned char* v_lds = lds + G_::KBYTES;
+
+  const int b = blockIdx.z;
+  const int hk = blockIdx.y;
+  const int cb = a.ncb - 1 - static_cast<int>(blockIdx.x);  // heaviest causal blocks first
+  const int n = a.seqlens_k[b];
+  const int q0 = a.cu_q[b];
+  const int L = a.cu_q[b + 1] - q0;
+  const int g = a.g;
+  const int ncols = L * g;
+  const int col0 = cb * 16 * W;
+  if (col0 >= ncols) return;
+  const int last_col = min(col0 + 16 * W, ncols) - 1;
+  const int jmax = column_limit(last_col, ncols, g, n, L, a.causal);
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int G = lane >> 4;
+  const int col = col0 + 16 * wave + (lane & 15);
+  const bool exists = col < ncols;
+  const int lim = exists ? column_limit(col, ncols, g, n, L, a.causal) : 0;
+  const int64_t rh = static_cast<int64_t>(q0 + col / g) * a.hq + hk * g + col % g;
+  QOps<T, D> q, dout;
+  row_operands_global<T, D>(a.q, rh, exists, q);
+  row_operands_global<T, D>(ba.dout, rh, exists, dout);
+  const float lse_u = (exists && lim > 0) ? lse_units<T>(ba.lse[rh]) : 0.f;
+  const float dlt = exists ? ba.delta[rh] : 0.f;
+
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.mbps;
+  const Append none;
+  for (int j0 = 0; j0 < jmax; j0 += KT) {
+    __syncthreads();
+    load_tile<T, D, W, false>(a, bt, hk, j0, jmax, k_lds, v_lds, none);
+    __syncthreads();
+    f32x4 s[G_::MT], dp[G_::MT];
+    {
+      KOps<T, D> op;
+      row_operands_lds<T, D>(k_lds, G_::KPITCH, op);
+      qk_tile<T, D>(op, q, s);
+      row_operands_lds<T, D>(v_lds, G_::VPITCH, op);
+      qk_tile<T, D>(op, dout, dp);
+    }
+#pragma unroll
+    for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = j0 + 16 * mt + 4 * G + i;
+        const bool vis = key < lim;
+        const float p = vis ? pkv_exp<T>(fmaf(s[mt][i], a.mul, -lse_u)) : 0.f;
+        s[mt][i] = vis ? p * (dp[mt][i] - dlt) : 0.f;  // dS^T
+      }
+    if constexpr (T::EB == 2) {
+#pragma unroll
+      for (int dt = 0; dt < G_::DT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < KT / 32; ++ks) {
+          const u32x4 kt = v_operand_bf16(k_lds, G_::KPITCH, ks, dt);
+          acc[dt] = mfma_bf16(kt, pack_bf16(s[2 * ks], s[2 * ks + 1]), acc[dt]);
+        }
+    } else {
+      const unsigned char* colp = k_lds + 4 * (lane & 15);
+#pragma unroll
+      for (int dt = 0; dt < G_::DT; ++dt)
+#pragma unroll
+        for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float kt = *reinterpret_cast<const float*>(colp + (16 * mt + 4 * G + i) * G_::KPITCH + 4 * 16 * dt);
+            acc[dt] = mfma_f32(kt, s[mt][i], acc[dt]);
+          }
+    }
+  }
+  if (exists) store_grad<T, D>(ba.dq, rh * D, acc, ba.scale);
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv: per key, over 32-column steps in ascending order:
+//   S = Q K^T, dP = dO V^T (columns as M, keys as N),
+//   P = exp(S * mul - lse), dS = P (dP - delta) (0 where the key is invisible),
+//   dV^T += dO^T P, dK^T += Q^T dS (head dim as M, columns as the k-dimension:
+//   k-slot 8G + e <-> column 4G + e (e < 4) or 16 + 4G + (e - 4)).
+// ---------------------------------------------------------------------------
+constexpr int kBwdCols = 32;  // columns per step of the dk/dv kernel
+
+template <class T, int D>
+struct ColTile {
+  static constexpr int ROW_BYTES = D * T::EB;
+  static constexpr int PITCH = ROW_BYTES + 32;  // the transposing read's bank-friendly pitch
+  static constexpr int BYTES = kBwdCols * PITCH;
+  static constexpr int CPR = ROW_BYTES / 16;
+  static constexpr int NK = ROW_BYTES / 64;
+};
+
+template <class T, int D, int W>
+__global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
+  const AttnArgs& a = ba.f;
+  using C_ = ColTile<T, D>;
+  constexpr int NK = C_::NK;
+  constexpr int DT = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C_::BYTES + 2 * kBwdCols * sizeof(float)];
+  unsigned char* q_lds = lds;
+  unsigned char* do_lds = lds + C_::BYTES;
+  float* lse_lds = reinterpret_cast<float*>(lds + 2 * C_::BYTES);
+  float* dl_lds = lse_lds + kBwdCols;
+
+  const int b = blockIdx.z;
+  const int hk = blockIdx.y;
+  const int key0 = static_cast<int>(blockIdx.x) * 16 * W;
+  const int n = a.seqlens_k[b];
+  if (key0 >= n) return;
+  const int q0 = a.cu_q[b];
+  const int L = a.cu_q[b + 1] - q0;
+  const int g = a.g;
+  const int ncols = L * g;
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int G = lane >> 4;
+  const int key = key0 + 16 * wave + (lane & 15);
+  const bool kin = key < n;
+
+  // This lane's key as the N operand of S and dP: bytes [64k + 16G, +16) of its K and V rows.
+  u32x4 kb[NK], vb[NK];
+  {
+    const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.mbps;
+    const int kc = min(key, n - 1);
+    const int bi = div_block(kc, a.bs_mul, a.bs_shift);
+    const int64_t blk = bt[bi];
+    const int64_t slot = kc - bi * a.bs;
+    const unsigned char* kp = static_cast<const unsigned char*>(a.k) + (blk * a.kbs + slot * a.kss + static_cast<int64_t>(hk) * a.khs) * T::EB + 16 * G;
+    const unsigned char* vp = static_cast<const unsigned char*>(a.v) + (blk * a.vbs + slot * a.vss + static_cast<int64_t>(hk) * a.vhs) * T::EB + 16 * G;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      kb[k] = kin ? *reinterpret_cast<const u32x4*>(kp + 64 * k) : u32x4{0, 0, 0, 0};
+      vb[k] = kin ? *reinterpret_cast<const u32x4*>(vp + 64 * k) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // Columns before c_start cannot see key0 (causal); the step grid stays at multiples of 32 from column 0.
+  int c_start = 0;
+  if (a.causal) {
+    const int r_min = max(key0 - (n - L), 0);
+    c_start = (min(r_min, L) * g) & ~(kBwdCols - 1);
+  }
+
+  f32x4 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int c0 = c_start; c0 < ncols; c0 += kBwdCols) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kBwdCols * C_::CPR; i += 64 * W) {
+      const int row = i / C_::CPR, part = i % C_::CPR;
+      const int c = c0 + row;
+      u32x4 xq = {0, 0, 0, 0}, xd = {0, 0, 0, 0};
+      if (c < ncols) {
+        const int64_t off = (static_cast<int64_t>(q0 + c / g) * a.hq + hk * g + c % g) * D * T::EB + 16 * part;
+        xq = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(a.q) + off);
+        xd = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(ba.dout) + off);
+      }
+      *reinterpret_cast<u32x4*>(q_lds + row * C_::PITCH + 16 * part) = xq;
+      *reinterpret_cast<u32x4*>(do_lds + row * C_::PITCH + 16 * part) = xd;
+    }
+    if (threadIdx.x < kBwdCols) {
+      const int c = c0 + threadIdx.x;
+      float lu = 0.f, dl = 0.f;
+      if (c < ncols) {
+        const int64_t rh = static_cast<int64_t>(q0 + c / g) * a.hq + hk * g + c % g;
+        if (column_limit(c, ncols, g, n, L, a.causal) > 0) lu = lse_units<T>(ba.lse[rh]);
+        dl = ba.delta[rh];
+      }
+      lse_lds[threadIdx.x] = lu;
+      dl_lds[threadIdx.x] = dl;
+    }
+    __syncthreads();
+
+    f32x4 s[2], dp[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      u32x4 x[NK];
+      const unsigned char* rq = q_lds + (16 * ct + (lane & 15)) * C_::PITCH + 16 * G;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) x[k] = *reinterpret_cast<const u32x4*>(rq + 64 * k);
+      s[ct] = dot_tile<T, NK>(x, kb);
+      const unsigned char* rd = do_lds + (16 * ct + (lane & 15)) * C_::PITCH + 16 * G;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) x[k] = *reinterpret_cast<const u32x4*>(rd + 64 * k);
+      dp[ct] = dot_tile<T, NK>(x, vb);
+    }
+    // s[ct][i] and dp[ct][i] at lane l: key l%16 of the wave, column c0 + 16 ct + 4G + i.
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lc = 16 * ct + 4 * G + i;
+        const int c = c0 + lc;
+        const bool vis = kin && c < ncols && key < column_limit(c, ncols, g, n, L, a.causal);
+        const float p = vis ? pkv_exp<T>(fmaf(s[ct][i], a.mul, -lse_lds[lc])) : 0.f;
+        dp[ct][i] = vis ? p * (dp[ct][i] - dl_lds[lc]) : 0.f;  // dS
+        s[ct][i] = p;                                         // P
+      }
+    if constexpr (T::EB == 2) {
+      const u32x4 pp = pack_bf16(s[0], s[1]);
+      const u32x4 pd = pack_bf16(dp[0], dp[1]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt] = mfma_bf16(v_operand_bf16(do_lds, C_::PITCH, 0, dt), pp, dv[dt]);
+        dk[dt] = mfma_bf16(v_operand_bf16(q_lds, C_::PITCH, 0, dt), pd, dk[dt]);
+      }
+    } else {
+      // fp32 step (ct, i): k-slot G <-> column 16 ct + 4G + i.
+      const int dcol = 4 * (lane & 15);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * ct + 4 * G + i;
+            const float xo = *reinterpret_cast<const float*>(do_lds + row * C_::PITCH + 4 * 16 * dt + dcol);
+            const float xq = *reinterpret_cast<const float*>(q_lds + row * C_::PITCH + 4 * 16 * dt + dcol);
+            dv[dt] = mfma_f32(xo, s[ct][i], dv[dt]);
+            dk[dt] = mfma_f32(xq, dp[ct][i], dk[dt]);
+          }
+    }
+  }
+
+  if (kin) {
+    const int64_t kr = (static_cast<int64_t>(ba.cu_k[b]) + key) * (a.hq / g) + hk;
+    store_grad<T, D>(ba.dk, kr * D, dk, ba.scale);
+    store_grad<T, D>(ba.dv, kr * D, dv, 1.0f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <class T, int D>
+static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& pl, hipStream_t stream) {
+  constexpr int W = 4;
+  const int64_t pairs = pl.total_q * a.f.hq;
+  if (pairs > 0) {
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(static_cast<unsigned>((pairs + 15) / 16)), dim3(256), 0, stream,
+                       a, pairs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.f.ncb > 0) {
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, W>), dim3(a.f.ncb, pl.hk, pl.batch), dim3(64 * W), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (a.nkb > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, W>), dim3(a.nkb, pl.hk, pl.batch), dim3(64 * W), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdArgs& a, const BwdPlan& pl, int dtype, int d, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (dtype == 1) return d == 128 ? launch_bwd_t<TBf16, 128>(a, pl, stream) : launch_bwd_t<TBf16, 64>(a, pl, stream);
+  return d == 128 ? launch_bwd_t<TF32, 128>(a, pl, stream) : launch_bwd_t<TF32, 64>(a, pl, stream);
+}
+
+}  // namespace pkv

@@ -88,7 +88,30 @@ __device__ __forceinline__ int div_block(int j, uint32_t mul, int shift) {
   return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(j)) * mul) >> shift);
 }
 
+// Arguments of the backward kernels.  `f` carries the forward's inputs
+// (q, caches, table, lengths, strides, GQA factor, block-size divisor,
+// causal flag; f.mul is the score multiplier of the forward).
+struct BwdArgs {
+  AttnArgs f;
+  const int32_t* cu_k;  // [batch + 1] row offsets of each sequence's keys in dk/dv
+  const void* out;      // forward output [total_q, Hq, d]
+  const float* lse;     // forward natural-log LSE [total_q, Hq]
+  const void* dout;     // cotangent of out [total_q, Hq, d]
+  void* dq;             // [total_q, Hq, d]
+  void* dk;             // [total_k, Hkv, d]
+  void* dv;             // [total_k, Hkv, d]
+  float* delta;         // workspace [total_q, Hq]: <dout, out> per (row, head)
+  float scale;          // softmax scale (multiplies the dq and dk sums)
+  int32_t nkb;          // key blocks per (sequence, KV head) of the dk/dv kernel
+};
+
+struct BwdPlan {
+  int batch, hk;
+  int64_t total_q;
+};
+
 hipError_t launch_attention(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream);
+hipError_t launch_backward(const BwdArgs& a, const BwdPlan& pl, int dtype, int d, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, int elem_bytes, int64_t total_new, hipStream_t stream);
 
 }  // namespace pkv

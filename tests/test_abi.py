@@ -98,3 +98,36 @@ def test_options_roundtrip_and_errors():
     assert L.pkv_set_option(pkv.PKV_OPT_PATH, 5) == -7
     assert L.pkv_set_option(99, 0) == -7
     assert L.pkv_error_string(-4).decode() == "misaligned pointer or stride"
+
+
+def test_backward_rejects_bad_arguments_before_launch():
+    L = pkv.lib()
+    lay = good_layout(total_q=2)
+    args = dict(q=16, k=16, v=32, bt=64, sk=64, cuq=64, cuk=64, total_k=10, causal=1, scale=0.1,
+                out=48, lse=64, dout=80, dq=96, dk=112, dv=128)
+
+    def call(**over):
+        a = dict(args, **over)
+        return L.pkv_attn_backward(a["q"], a["k"], a["v"], ctypes.byref(lay), a["bt"], a["sk"], a["cuq"], a["cuk"],
+                                   a["total_k"], a["causal"], a["scale"], a["out"], a["lse"], a["dout"], a["dq"],
+                                   a["dk"], a["dv"], None, 0, None)
+
+    assert call(dout=None) == -1
+    assert call(dk=None) == -1
+    assert call(cuk=None) == -1
+    assert call(dq=8) == -4
+    assert call(dout=24) == -4
+    assert call(scale=0.0) == -2
+    assert call(scale=float("inf")) == -2
+    assert call(total_k=-1) == -2
+    # a caller workspace that is too small is rejected before any launch
+    rc = L.pkv_attn_backward(16, 16, 32, ctypes.byref(lay), 64, 64, 64, 64, 10, 1, 0.1, 48, 64, 80, 96, 112, 128,
+                             256, 4, None)
+    assert rc == -5
+
+
+def test_backward_workspace_size():
+    L = pkv.lib()
+    lay = good_layout(total_q=100)
+    assert L.pkv_attn_backward_workspace_size(ctypes.byref(lay)) == -(-100 * 16 * 4 // 256) * 256
+    assert L.pkv_attn_backward_workspace_size(ctypes.byref(good_layout(head_dim=3))) == 0
