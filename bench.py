@@ -11,7 +11,8 @@ Prints one JSON line: value = KV bytes read per second (GB/s) over the timed
 steps, the roofline of the attention launch (bytes it must move / its HIP-event
 duration vs 8 TB/s HBM), the oracle's throughput on a bounded sample of the
 same work on the host's cores, a prefill figure (TFLOP/s of the full causal
-prefill of batch 8 x 8192 tokens, Hq 16, Hkv 4), and bitwise checks.
+prefill of batch 8 x 8192 tokens, Hq 16, Hkv 4) and of its backward, and
+bitwise checks.
 """
 
 from __future__ import annotations
@@ -168,7 +169,7 @@ def main():
     del ws, p_out, p_lse
 
     if not args.no_prefill:
-        result["prefill"] = bench_prefill(torch, pkv, gen)
+        result["prefill"], result["backward"] = bench_prefill(torch, pkv, gen)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale)
     print(json.dumps(result), flush=True)
@@ -225,11 +226,39 @@ def bench_prefill(torch, pkv, gen, reps: int = 3):
     ms = e0.elapsed_time(e1) / reps
     flops = 4.0 * D * HQ * B * (S * (S + 1) / 2)
     tf = flops / (ms * 1e-3) / 1e12
-    del pool
+    fwd = {"workload": "full causal prefill batch 8 x 8192, Hq 16, Hkv 4, d 128, bs 16",
+           "ms": round(ms, 3), "tflops": round(tf, 2), "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+           "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": flops}
+
+    # Backward of the same prefill: dq, dk, dv for a seeded N(0,1) cotangent.
+    # Algorithmic FLOPs: the five products dP, dV, dK, dQ and the recomputed S
+    # over the causal pairs, 2.5x the forward's two.
+    out, lse = call()
+    dout = gen.randn((B * S, HQ, D), "bf16", generator=g, device=dev)
+    cuk = torch.arange(0, B * S + 1, S, dtype=torch.int32, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty((B * S, HK, D), dtype=q.dtype, device=dev)
+    dv = torch.empty_like(dk)
+
+    def bwd():
+        return pkv.attn_backward(q, pool.k, pool.v, bt, sk, cu, True, scale, out, lse, dout, max_seqlen_q=S,
+                                 max_seqlen_k=S, cu_seqlens_k=cuk, total_k=B * S, dq=dq, dk=dk, dv=dv)
+
+    bwd()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        bwd()
+    e1.record()
+    e1.synchronize()
+    bms = e0.elapsed_time(e1) / reps
+    bflops = 2.5 * flops
+    btf = bflops / (bms * 1e-3) / 1e12
+    bwd_res = {"workload": "backward of the same prefill (dq, dk, dv)", "ms": round(bms, 3),
+               "tflops": round(btf, 2), "frac": round(btf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": bflops}
+    del pool, out, lse, dout, dq, dk, dv
     torch.cuda.empty_cache()
-    return {"workload": "full causal prefill batch 8 x 8192, Hq 16, Hkv 4, d 128, bs 16",
-            "ms": round(ms, 3), "tflops": round(tf, 2), "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": flops}
+    return fwd, bwd_res
 
 
 def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, budget_s: float = 12.0):

@@ -241,8 +241,10 @@ int pkv_validate_layout(const pkv_layout* kv_strides);
  * which kernels run and how work is split.
  *   PKV_OPT_PATH          0 auto, 1 split (decode kernels + merge), 2 full (prefill kernel)
  *   PKV_OPT_SPLIT_CHUNKS  chunks handled by one split work item (0 = auto, 1..64)
+ *   PKV_OPT_FULL_KERNEL   bf16 full path: 0 auto, 1 pipelined 8-wave kernel (few long
+ *                         column blocks), 2 single-buffered 4-wave kernel (many blocks)
  */
-enum pkv_option { PKV_OPT_PATH = 1, PKV_OPT_SPLIT_CHUNKS = 2 };
+enum pkv_option { PKV_OPT_PATH = 1, PKV_OPT_SPLIT_CHUNKS = 2, PKV_OPT_FULL_KERNEL = 3 };
 int pkv_set_option(int option, int64_t value);
 int64_t pkv_get_option(int option);
 

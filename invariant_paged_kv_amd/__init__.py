@@ -24,7 +24,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_F32, PKV_BF16 = 0, 1
-PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS = 1, 2
+PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL = 1, 2, 3
 CHUNK_KEYS = 512
 TILE_KEYS = 64
 
@@ -342,12 +342,15 @@ def get_option(option: int) -> int:
 class options:
     """Context manager that sets library options and restores them on exit."""
 
-    def __init__(self, path: Optional[int] = None, split_chunks: Optional[int] = None):
+    def __init__(self, path: Optional[int] = None, split_chunks: Optional[int] = None,
+                 full_kernel: Optional[int] = None):
         self._want = {}
         if path is not None:
             self._want[PKV_OPT_PATH] = path
         if split_chunks is not None:
             self._want[PKV_OPT_SPLIT_CHUNKS] = split_chunks
+        if full_kernel is not None:
+            self._want[PKV_OPT_FULL_KERNEL] = full_kernel
         self._old = {}
 
     def __enter__(self):

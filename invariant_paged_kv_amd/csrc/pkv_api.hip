@@ -24,6 +24,7 @@ static_assert(PKV_CHUNK_KEYS == 512 && PKV_TILE_KEYS == 64, "header constants mu
 thread_local char g_msg[512] = "";
 std::atomic<int64_t> g_opt_path{0};
 std::atomic<int64_t> g_opt_split_chunks{0};
+std::atomic<int64_t> g_opt_full_kernel{0};
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -103,7 +104,17 @@ Plan make_plan(const pkv_layout& l) {
     full = full_items >= 512;
   }
   if (!full) waves = cols <= 16 ? 1 : 4;
-  const int cols_per_block = full ? 128 : 16 * waves;
+  // bf16 full path: with many column blocks, the single-buffered 4-wave kernel
+  // (three work groups per CU) beats the pipelined 8-wave one (one per CU);
+  // with few long blocks (long keys, few rows) the pipelined one wins.
+  bool full4 = false;
+  if (full && l.dtype == PKV_BF16) {
+    const int64_t opt = g_opt_full_kernel.load();
+    const int64_t blocks64 = static_cast<int64_t>(l.batch) * l.num_heads_k * ((cols + 63) / 64);
+    full4 = opt == 2 || (opt == 0 && blocks64 >= 2048);
+  }
+  p.lp.full4 = full4;
+  const int cols_per_block = full ? (full4 ? 64 : 128) : 16 * waves;
   p.ncb = static_cast<int>(std::max<int64_t>(1, (cols + cols_per_block - 1) / cols_per_block));
   int64_t cpi = g_opt_split_chunks.load();
   if (cpi <= 0) cpi = 1;
@@ -380,6 +391,10 @@ int pkv_set_option(int option, int64_t value) {
       if (value < 0 || value > 64) return fail(PKV_ERR_OPTION, "PKV_OPT_SPLIT_CHUNKS must be in 0..64");
       g_opt_split_chunks.store(value);
       return ok();
+    case PKV_OPT_FULL_KERNEL:
+      if (value < 0 || value > 2) return fail(PKV_ERR_OPTION, "PKV_OPT_FULL_KERNEL must be 0, 1 or 2");
+      g_opt_full_kernel.store(value);
+      return ok();
     default:
       return fail(PKV_ERR_OPTION, "unknown option %d", option);
   }
@@ -389,6 +404,7 @@ int64_t pkv_get_option(int option) {
   switch (option) {
     case PKV_OPT_PATH: return g_opt_path.load();
     case PKV_OPT_SPLIT_CHUNKS: return g_opt_split_chunks.load();
+    case PKV_OPT_FULL_KERNEL: return g_opt_full_kernel.load();
     default: return -1;
   }
 }

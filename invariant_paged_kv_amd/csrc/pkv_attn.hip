@@ -119,10 +119,14 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
       load_tile<T, D, W, APPEND>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
       __syncthreads();
       f32x4 s[NT][KT / 16];
-      KOps<T, D> kop;
-      k_operands_lds<T, D>(k_lds, kop);
+      if constexpr (NT == 1) {
+        qk_tile_lds<T, D>(k_lds, q[0], s[0]);  // one M tile of K operands live at a time
+      } else {
+        KOps<T, D> kop;
+        k_operands_lds<T, D>(k_lds, kop);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
+        for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
+      }
       softmax_pv_tile<T, D, NT>(st, s, lim, j0, a.mul, v_lds);
     }
 #pragma unroll
@@ -303,33 +307,6 @@ __device__ __forceinline__ void prefill_store(unsigned char* k_lds, unsigned cha
     const int row = qi / G_::CPR, part = qi % G_::CPR;
     *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = r.k[i];
     *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = r.v[i];
-  }
-}
-
-// QK^T with the K operands read from the LDS tile one M tile at a time (same
-// MFMA chain as qk_tile).
-template <class T, int D>
-__device__ __forceinline__ void qk_tile_lds(const unsigned char* k_lds, const QOps<T, D>& q, f32x4 (&s)[KT / 16]) {
-  using G_ = TileGeom<T, D>;
-  const int lane = lane_id();
-  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH + 16 * (lane >> 4);
-#pragma unroll
-  for (int mt = 0; mt < G_::MT; ++mt) {
-    KOps<T, D> kop;
-#pragma unroll
-    for (int k = 0; k < G_::NK; ++k) kop[0][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + 64 * k);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < G_::NK; ++k) {
-      if constexpr (T::EB == 2) {
-        acc = mfma_bf16(kop[0][k], q.v[k], acc);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc = mfma_f32(__uint_as_float(kop[0][k][e]), __uint_as_float(q.v[k][e]), acc);
-      }
-    }
-    s[mt] = acc;
   }
 }
 
@@ -616,7 +593,11 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   if (pl.full) {
     dim3 grid(a.ncb, pl.hk, pl.batch);
     if constexpr (T::EB == 2) {
-      hipLaunchKernelGGL((prefill_kernel<T, D, 8, APPEND>), grid, dim3(512), 0, stream, a);
+      if (pl.full4) {
+        hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, false, APPEND>), grid, dim3(256), 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((prefill_kernel<T, D, 8, APPEND>), grid, dim3(512), 0, stream, a);
+      }
     } else {
       hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false, APPEND>), grid, dim3(256), 0, stream, a);
     }

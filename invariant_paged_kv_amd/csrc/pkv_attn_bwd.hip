@@ -244,17 +244,77 @@ struct ColTile {
   static constexpr int NK = ROW_BYTES / 64;
 };
 
+// Register stage of one 32-column step: this thread's 16-byte pieces of the
+// Q and dO rows, and (threads < 32) one column's LSE (score units) and delta.
+template <class T, int D, int W>
+struct ColStage {
+  static constexpr int PER = kBwdCols * ColTile<T, D>::CPR / (64 * W);
+  u32x4 q[PER];
+  u32x4 d[PER];
+  float lu, dl;
+};
+
+template <class T, int D, int W>
+__device__ __forceinline__ void col_stage_load(const BwdArgs& ba, int q0, int hk, int ncols, int n, int L, int c0,
+                                               ColStage<T, D, W>& st) {
+  const AttnArgs& a = ba.f;
+  using C_ = ColTile<T, D>;
+  using S_ = ColStage<T, D, W>;
+  static_assert(S_::PER * 64 * W == kBwdCols * C_::CPR, "column tile pieces must split evenly over the work group");
+  const int g = a.g;
+#pragma unroll
+  for (int i = 0; i < S_::PER; ++i) {
+    const int qi = threadIdx.x + i * 64 * W;
+    const int row = qi / C_::CPR, part = qi % C_::CPR;
+    const int c = min(c0 + row, ncols - 1);  // columns past the end load a real row, then read as zero
+    const int64_t off = (static_cast<int64_t>(q0 + c / g) * a.hq + hk * g + c % g) * D * T::EB + 16 * part;
+    const bool in = c0 + row < ncols;
+    const u32x4 xq = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(a.q) + off);
+    const u32x4 xd = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(ba.dout) + off);
+    st.q[i] = in ? xq : u32x4{0, 0, 0, 0};
+    st.d[i] = in ? xd : u32x4{0, 0, 0, 0};
+  }
+  if (threadIdx.x < kBwdCols) {
+    const int c = c0 + threadIdx.x;
+    st.lu = 0.f;
+    st.dl = 0.f;
+    if (c < ncols) {
+      const int64_t rh = static_cast<int64_t>(q0 + c / g) * a.hq + hk * g + c % g;
+      if (column_limit(c, ncols, g, n, L, a.causal) > 0) st.lu = lse_units<T>(ba.lse[rh]);
+      st.dl = ba.delta[rh];
+    }
+  }
+}
+
+template <class T, int D, int W>
+__device__ __forceinline__ void col_stage_store(unsigned char* buf, const ColStage<T, D, W>& st) {
+  using C_ = ColTile<T, D>;
+  using S_ = ColStage<T, D, W>;
+#pragma unroll
+  for (int i = 0; i < S_::PER; ++i) {
+    const int qi = threadIdx.x + i * 64 * W;
+    const int row = qi / C_::CPR, part = qi % C_::CPR;
+    *reinterpret_cast<u32x4*>(buf + row * C_::PITCH + 16 * part) = st.q[i];
+    *reinterpret_cast<u32x4*>(buf + C_::BYTES + row * C_::PITCH + 16 * part) = st.d[i];
+  }
+  if (threadIdx.x < kBwdCols) {
+    float* f = reinterpret_cast<float*>(buf + 2 * C_::BYTES);
+    f[threadIdx.x] = st.lu;
+    f[kBwdCols + threadIdx.x] = st.dl;
+  }
+}
+
+// Each 32-column step is computed from one LDS buffer while the next step's
+// rows are in flight in registers; they go to the other buffer afterwards, and
+// one barrier per step separates the two.
 template <class T, int D, int W>
 __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
   const AttnArgs& a = ba.f;
   using C_ = ColTile<T, D>;
   constexpr int NK = C_::NK;
   constexpr int DT = D / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * C_::BYTES + 2 * kBwdCols * sizeof(float)];
-  unsigned char* q_lds = lds;
-  unsigned char* do_lds = lds + C_::BYTES;
-  float* lse_lds = reinterpret_cast<float*>(lds + 2 * C_::BYTES);
-  float* dl_lds = lse_lds + kBwdCols;
+  constexpr int BUF = 2 * C_::BYTES + 2 * kBwdCols * sizeof(float);
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
 
   const int b = blockIdx.z;
   const int hk = blockIdx.y;
@@ -271,6 +331,15 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
   const int G = lane >> 4;
   const int key = key0 + 16 * wave + (lane & 15);
   const bool kin = key < n;
+
+  // Columns before c_start cannot see key0 (causal); the step grid stays at multiples of 32 from column 0.
+  int c_start = 0;
+  if (a.causal) {
+    const int r_min = max(key0 - (n - L), 0);
+    c_start = (min(r_min, L) * g) & ~(kBwdCols - 1);
+  }
+  ColStage<T, D, W> stage;
+  if (c_start < ncols) col_stage_load<T, D, W>(ba, q0, hk, ncols, n, L, c_start, stage);
 
   // This lane's key as the N operand of S and dP: bytes [64k + 16G, +16) of its K and V rows.
   u32x4 kb[NK], vb[NK];
@@ -289,13 +358,6 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
     }
   }
 
-  // Columns before c_start cannot see key0 (causal); the step grid stays at multiples of 32 from column 0.
-  int c_start = 0;
-  if (a.causal) {
-    const int r_min = max(key0 - (n - L), 0);
-    c_start = (min(r_min, L) * g) & ~(kBwdCols - 1);
-  }
-
   f32x4 dk[DT], dv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -303,32 +365,16 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
     dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  if (c_start < ncols) col_stage_store<T, D, W>(lds, stage);
+  __syncthreads();
+  int cur = 0;
   for (int c0 = c_start; c0 < ncols; c0 += kBwdCols) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < kBwdCols * C_::CPR; i += 64 * W) {
-      const int row = i / C_::CPR, part = i % C_::CPR;
-      const int c = c0 + row;
-      u32x4 xq = {0, 0, 0, 0}, xd = {0, 0, 0, 0};
-      if (c < ncols) {
-        const int64_t off = (static_cast<int64_t>(q0 + c / g) * a.hq + hk * g + c % g) * D * T::EB + 16 * part;
-        xq = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(a.q) + off);
-        xd = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(ba.dout) + off);
-      }
-      *reinterpret_cast<u32x4*>(q_lds + row * C_::PITCH + 16 * part) = xq;
-      *reinterpret_cast<u32x4*>(do_lds + row * C_::PITCH + 16 * part) = xd;
-    }
-    if (threadIdx.x < kBwdCols) {
-      const int c = c0 + threadIdx.x;
-      float lu = 0.f, dl = 0.f;
-      if (c < ncols) {
-        const int64_t rh = static_cast<int64_t>(q0 + c / g) * a.hq + hk * g + c % g;
-        if (column_limit(c, ncols, g, n, L, a.causal) > 0) lu = lse_units<T>(ba.lse[rh]);
-        dl = ba.delta[rh];
-      }
-      lse_lds[threadIdx.x] = lu;
-      dl_lds[threadIdx.x] = dl;
-    }
-    __syncthreads();
+    const bool more = c0 + kBwdCols < ncols;
+    if (more) col_stage_load<T, D, W>(ba, q0, hk, ncols, n, L, c0 + kBwdCols, stage);
+    const unsigned char* q_lds = lds + cur * BUF;
+    const unsigned char* do_lds = q_lds + C_::BYTES;
+    const float* lse_lds = reinterpret_cast<const float*>(q_lds + 2 * C_::BYTES);
+    const float* dl_lds = lse_lds + kBwdCols;
 
     f32x4 s[2], dp[2];
 #pragma unroll
@@ -379,6 +425,9 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
             dk[dt] = mfma_f32(xq, dp[ct][i], dk[dt]);
           }
     }
+    if (more) col_stage_store<T, D, W>(lds + (cur ^ 1) * BUF, stage);
+    __syncthreads();
+    cur ^= 1;
   }
 
   if (kin) {

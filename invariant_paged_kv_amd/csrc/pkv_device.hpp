@@ -179,6 +179,33 @@ __device__ __forceinline__ void k_operands_lds(const unsigned char* k_lds, KOps<
       kop[mt][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + 64 * k);
 }
 
+// QK^T with the K operands read from the LDS tile one M tile at a time (same
+// MFMA chain as qk_tile).
+template <class T, int D>
+__device__ __forceinline__ void qk_tile_lds(const unsigned char* k_lds, const QOps<T, D>& q, f32x4 (&s)[KT / 16]) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH + 16 * (lane >> 4);
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt) {
+    KOps<T, D> kop;
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) kop[0][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + 64 * k);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) {
+      if constexpr (T::EB == 2) {
+        acc = mfma_bf16(kop[0][k], q.v[k], acc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = mfma_f32(__uint_as_float(kop[0][k][e]), __uint_as_float(q.v[k][e]), acc);
+      }
+    }
+    s[mt] = acc;
+  }
+}
+
 // V^T operand (A) of PV step ks for d-tile dt, bf16: slot 8G+e <-> key
 // 32ks + 4G + e (e < 4) and 32ks + 16 + 4G + (e - 4) (e >= 4), head-dim row
 // 16dt + l%16.  ds_read_b64_tr_b16 turns four 8-byte row pieces of the 16

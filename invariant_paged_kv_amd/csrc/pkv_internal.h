@@ -51,6 +51,7 @@ struct MergeArgs {
 
 struct LaunchPlan {
   bool full;       // prefill kernel (true) or split kernels + merge (false)
+  bool full4;      // full path, bf16: 4-wave single-buffered kernel instead of the 8-wave pipelined one
   bool append;     // fused append of k_new / v_new
   int waves;       // split path: waves per work group (1 or 4)
   int items;       // split path: work items per column block along the keys

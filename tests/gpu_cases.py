@@ -51,13 +51,13 @@ class Case:
 
 
 def run(case: Case, pool: Optional[gen.PagedKV] = None, block_table=None, q=None, path=None,
-        split_chunks=None, scale=None, seqlens=None, cu=None, causal=None):
+        split_chunks=None, scale=None, seqlens=None, cu=None, causal=None, full_kernel=None):
     pool = pool or case.pool
     bt = case.block_table if block_table is None else block_table
     q = case.q if q is None else q
     sl = case.seqlens if seqlens is None else seqlens
     cul = case.cu if cu is None else cu
-    with pkv.options(path=path, split_chunks=split_chunks):
+    with pkv.options(path=path, split_chunks=split_chunks, full_kernel=full_kernel):
         out, lse = pkv.attn_forward(
             q, pool.k, pool.v, bt, torch.tensor(sl, dtype=torch.int32, device=DEV),
             torch.tensor(cul, dtype=torch.int32, device=DEV),

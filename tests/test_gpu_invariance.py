@@ -52,6 +52,21 @@ def test_split_count_and_path_invariance(dtype, d):
     for path in (1, 2):
         for split in (1, 2, 3, 7, 64):
             gc.assert_bitwise(gc.run(case, path=path, split_chunks=split), ref, f"path {path} split {split}")
+    for fk in (1, 2):
+        gc.assert_bitwise(gc.run(case, path=2, full_kernel=fk), ref, f"full path, kernel {fk}")
+
+
+@pytest.mark.parametrize("layout", ["interleaved", "contiguous"])
+def test_full_path_kernels_agree(layout):
+    """The two bf16 full-path kernels (pipelined 8-wave, single-buffered 4-wave) and
+    the split path give the same bits on a chunked prefill with ragged rows."""
+    announce(f"full-path kernels {layout}")
+    lens, seqlens = [300, 17, 129, 64], [900, 17, 700, 1030]
+    case = gc.make_case(3010, "bf16", 4, 16, 4, 128, 16, max(seqlens), layout, True, lens, seqlens)
+    ref = gc.run(case, path=2, full_kernel=1)
+    gc.check_oracle(case, *ref, seq_ids=[1, 3])
+    gc.assert_bitwise(gc.run(case, path=2, full_kernel=2), ref, "4-wave vs 8-wave full kernel")
+    gc.assert_bitwise(gc.run(case, path=1), ref, "split vs full")
 
 
 def test_permuted_block_table():
@@ -77,6 +92,8 @@ def test_unread_memory_is_never_read():
     gc.assert_bitwise(gc.run(case, block_table=bt2), ref, "poisoned pool and table tail")
     for path in (1, 2):
         gc.assert_bitwise(gc.run(case, block_table=bt2, path=path), ref, f"poisoned, path {path}")
+    for fk in (1, 2):
+        gc.assert_bitwise(gc.run(case, block_table=bt2, path=2, full_kernel=fk), ref, f"poisoned, full kernel {fk}")
 
 
 def test_run_to_run_determinism():
