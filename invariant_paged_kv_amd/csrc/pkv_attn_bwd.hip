@@ -193,15 +193,22 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
       row_operands_lds<T, D>(v_lds, G_::VPITCH, op);
       qk_tile<T, D>(op, dout, dp);
     }
+    if (__all(j0 + KT <= lim)) {  // the whole tile is visible to every lane: no mask
 #pragma unroll
-    for (int mt = 0; mt < G_::MT; ++mt)
+      for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = j0 + 16 * mt + 4 * G + i;
-        const bool vis = key < lim;
-        const float p = vis ? pkv_exp<T>(fmaf(s[mt][i], a.mul, -lse_u)) : 0.f;
-        s[mt][i] = vis ? p * (dp[mt][i] - dlt) : 0.f;  // dS^T
-      }
+        for (int i = 0; i < 4; ++i) s[mt][i] = pkv_exp<T>(fmaf(s[mt][i], a.mul, -lse_u)) * (dp[mt][i] - dlt);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j0 + 16 * mt + 4 * G + i;
+          const bool vis = key < lim;
+          const float p = vis ? pkv_exp<T>(fmaf(s[mt][i], a.mul, -lse_u)) : 0.f;
+          s[mt][i] = vis ? p * (dp[mt][i] - dlt) : 0.f;  // dS^T
+        }
+    }
     if constexpr (T::EB == 2) {
 #pragma unroll
       for (int dt = 0; dt < G_::DT; ++dt)
@@ -308,7 +315,7 @@ __device__ __forceinline__ void col_stage_store(unsigned char* buf, const ColSta
 // rows are in flight in registers; they go to the other buffer afterwards, and
 // one barrier per step separates the two.
 template <class T, int D, int W>
-__global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
+__global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(BwdArgs ba) {
   const AttnArgs& a = ba.f;
   using C_ = ColTile<T, D>;
   constexpr int NK = C_::NK;
@@ -338,6 +345,9 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
     const int r_min = max(key0 - (n - L), 0);
     c_start = (min(r_min, L) * g) & ~(kBwdCols - 1);
   }
+  // This lane's key is visible to column c (row c / g at position n - L + c / g)
+  // iff c >= c_vis: key <= n - L + floor(c / g)  <=>  c >= (key - n + L) * g.
+  const int c_vis = !kin ? INT_MAX : (a.causal ? max(key - (n - L), 0) * g : 0);
   ColStage<T, D, W> stage;
   if (c_start < ncols) col_stage_load<T, D, W>(ba, q0, hk, ncols, n, L, c_start, stage);
 
@@ -390,17 +400,31 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdArgs ba) {
       dp[ct] = dot_tile<T, NK>(x, vb);
     }
     // s[ct][i] and dp[ct][i] at lane l: key l%16 of the wave, column c0 + 16 ct + 4G + i.
+    // When every lane sees the whole step the per-element mask is skipped (it
+    // would select nothing).
+    if (__all(c0 >= c_vis) && c0 + kBwdCols <= ncols) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int lc = 16 * ct + 4 * G + i;
-        const int c = c0 + lc;
-        const bool vis = kin && c < ncols && key < column_limit(c, ncols, g, n, L, a.causal);
-        const float p = vis ? pkv_exp<T>(fmaf(s[ct][i], a.mul, -lse_lds[lc])) : 0.f;
-        dp[ct][i] = vis ? p * (dp[ct][i] - dl_lds[lc]) : 0.f;  // dS
-        s[ct][i] = p;                                         // P
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int lc = 16 * ct + 4 * G + i;
+          const float p = pkv_exp<T>(fmaf(s[ct][i], a.mul, -lse_lds[lc]));
+          dp[ct][i] = p * (dp[ct][i] - dl_lds[lc]);  // dS
+          s[ct][i] = p;                              // P
+        }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int lc = 16 * ct + 4 * G + i;
+          const int c = c0 + lc;
+          const bool vis = c >= c_vis && c < ncols;
+          const float p = vis ? pkv_exp<T>(fmaf(s[ct][i], a.mul, -lse_lds[lc])) : 0.f;
+          dp[ct][i] = vis ? p * (dp[ct][i] - dl_lds[lc]) : 0.f;  // dS
+          s[ct][i] = p;                                         // P
+        }
+    }
     if constexpr (T::EB == 2) {
       const u32x4 pp = pack_bf16(s[0], s[1]);
       const u32x4 pd = pack_bf16(dp[0], dp[1]);
