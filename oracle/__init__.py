@@ -25,6 +25,8 @@ from .paged_kv import (  # noqa: F401
     attention,
     bf16_bits_to_f64,
     cache_write,
+    fp8e4m3_bits_to_f64,
+    gather_kv,
     gather_sequence,
     masked_softmax,
     scores,

@@ -38,7 +38,7 @@ from typing import Sequence, Tuple
 
 import numpy as np
 
-from .paged_kv import Layout, _as_f64, gather_sequence, kv_head_of, masked_softmax, scores, visible_keys
+from .paged_kv import Layout, _as_f64, gather_kv, kv_head_of, masked_softmax, scores, visible_keys
 
 
 def cu_seqlens_k_of(seqlens_k: Sequence[int]) -> np.ndarray:
@@ -62,8 +62,7 @@ def _sequences(q, k_flat, v_flat, layout, block_table, seqlens_k, cu_seqlens_q, 
         r0, r1 = int(cu[b]), int(cu[b + 1])
         if n > bt.shape[1] * bs:
             raise ValueError(f"seqlens_k[{b}]={n} exceeds the block table")
-        K = gather_sequence(k_flat, layout.dtype, layout.k_offset, layout.k_strides, bt[b], n, bs, Hk, d)
-        V = gather_sequence(v_flat, layout.dtype, layout.v_offset, layout.v_strides, bt[b], n, bs, Hk, d)
+        K, V = gather_kv(k_flat, v_flat, layout, bt[b], n)
         yield b, r0, r1, n, K, V, visible_keys(n, r1 - r0, causal)
 
 

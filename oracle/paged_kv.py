@@ -35,13 +35,13 @@ Readings taken where the pages are silent (each one is listed in the design doc):
   call's own query rows.
 
 Everything is float64.  bf16 storage is passed as raw ``uint16`` bit patterns
-and widened exactly.
+and FP8 E4M3 storage as raw ``uint8`` bytes; both are widened exactly.
 """
 
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Sequence, Tuple
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -66,6 +66,16 @@ class Layout:
     k_strides: Tuple[int, int, int]
     v_offset: int
     v_strides: Tuple[int, int, int]
+    # Stored K/V element type if it differs from the queries' ("fp8e4m3": OCP
+    # FP8 E4M3 bytes), and the per-tensor factors that turn stored values into
+    # K and V (K = stored * k_scale, V = stored * v_scale).
+    kv_dtype: Optional[str] = None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def stored_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -78,9 +88,28 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u32.view(np.float32).astype(np.float64)
 
 
+def fp8e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 bytes (uint8) as float64.
+
+    The format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+    infinities; exponent 0 encodes subnormals m * 2^-9, and exponent 15 with
+    mantissa 7 is NaN (so the largest finite magnitude is 1.75 * 2^8 = 448).
+    """
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    normal = sign * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = sign * m * 2.0 ** -9
+    out = np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
 def _as_f64(values: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f64(values)
+    if dtype == "fp8e4m3":
+        return fp8e4m3_bits_to_f64(values)
     if dtype == "f32":
         return np.asarray(values, dtype=np.float32).astype(np.float64)
     if dtype == "f64":  # exact float64 inputs (finite-difference checks)
@@ -130,6 +159,19 @@ def gather_sequence(flat: np.ndarray, dtype: str, offset: int,
                      np.arange(num_heads_k, dtype=np.int64)[None, :, None],
                      np.arange(head_dim, dtype=np.int64)[None, None, :])
     return _as_f64(np.asarray(flat)[idx], dtype)
+
+
+def gather_kv(k_flat: np.ndarray, v_flat: np.ndarray, layout: Layout,
+              block_table_row: np.ndarray, n: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense float64 ``K, V`` (``[n, nheads_k, d]``) of one sequence.
+
+    Stored values are widened exactly and multiplied by the layout's K and V
+    scales (1 unless the cache stores scaled values, e.g. FP8).
+    """
+    args = (block_table_row, n, layout.block_size, layout.num_heads_k, layout.head_dim)
+    K = gather_sequence(k_flat, layout.stored_dtype, layout.k_offset, layout.k_strides, *args)
+    V = gather_sequence(v_flat, layout.stored_dtype, layout.v_offset, layout.v_strides, *args)
+    return K * layout.k_scale, V * layout.v_scale
 
 
 def row_positions(n: int, L: int) -> np.ndarray:
@@ -190,10 +232,7 @@ def attention(q: np.ndarray, k_flat: np.ndarray, v_flat: np.ndarray,
             continue
         if n > bt.shape[1] * bs:
             raise ValueError(f"seqlens_k[{b}]={n} exceeds the block table")
-        K = gather_sequence(k_flat, layout.dtype, layout.k_offset, layout.k_strides,
-                            bt[b], n, bs, Hk, d)
-        V = gather_sequence(v_flat, layout.dtype, layout.v_offset, layout.v_strides,
-                            bt[b], n, bs, Hk, d)
+        K, V = gather_kv(k_flat, v_flat, layout, bt[b], n)
         vis = visible_keys(n, L, causal)                    # [L, n]
         for h in range(Hq):
             hk = kv_head_of(h, Hq, Hk)

@@ -29,7 +29,8 @@ from typing import List, Optional, Sequence
 
 import torch
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+FP8_NAN_BYTE = 0x7F  # an OCP FP8 E4M3 NaN
 
 
 @dataclass
@@ -76,9 +77,9 @@ def new_pool(num_blocks: int, block_size: int, nheads_k: int, d: int, dtype: str
         buf = torch.randn(shape, dtype=torch.float32, device=device,
                           generator=generator).to(tdt)
     elif fill == "zeros":
-        buf = torch.zeros(shape, dtype=tdt, device=device)
+        buf = torch.zeros(shape, dtype=torch.float32, device=device).to(tdt)
     elif fill == "nan":
-        buf = torch.full(shape, float("nan"), dtype=tdt, device=device)
+        buf = torch.full(shape, float("nan"), dtype=torch.float32, device=device).to(tdt)
     else:
         raise ValueError(fill)
     if layout == "interleaved":
@@ -119,7 +120,7 @@ def cu_from_lengths(lengths: Sequence[int], device="cpu") -> torch.Tensor:
 
 def randn(shape, dtype: str, generator: Optional[torch.Generator] = None,
           device="cpu") -> torch.Tensor:
-    """N(0, 1) values drawn in float32 and rounded to ``dtype``."""
+    """N(0, 1) values drawn in float32 and rounded to ``dtype`` (round to nearest even)."""
     return torch.randn(shape, dtype=torch.float32, generator=generator,
                        device=device).to(DTYPES[dtype])
 
@@ -169,9 +170,14 @@ def poison_unused(pool: PagedKV, block_table: torch.Tensor,
                 tail.append((int(bt[b, nblk - 1]), int(n) % bs))
     unused = (~used).nonzero().flatten().to(pool.k.device)
     for t in (pool.k, pool.v):
-        t.index_fill_(0, unused, value)
+        if t.dtype == torch.float8_e4m3fn:   # fill the bytes: FP8 NaN for a NaN value
+            t = t.view(torch.uint8)
+            value_t = FP8_NAN_BYTE if math.isnan(value) else int(torch.tensor(value).to(torch.float8_e4m3fn).view(torch.uint8))
+        else:
+            value_t = value
+        t.index_fill_(0, unused, value_t)
         for blk, start in tail:
-            t[blk, start:].fill_(value)
+            t[blk, start:].fill_(value_t)
 
 
 def poison_table_tail(block_table: torch.Tensor, seqlens_k: Sequence[int],
