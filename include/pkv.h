@@ -56,12 +56,20 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 #define PKV_CHUNK_KEYS 512  /* keys per chunk: the unit partials are merged in */
 #define PKV_TILE_KEYS 64    /* keys per tile inside a chunk */
 
-/* Element type of q, the cache, new K/V and out.  lse is always fp32. */
-enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 };
+/*
+ * Element types.  PKV_F32 / PKV_BF16: q, the cache, new K/V and out share the
+ * type.  PKV_FP8_E4M3: q and out are bf16; the cache and new K/V rows hold OCP
+ * FP8 E4M3 bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; NaN
+ * 0x7f/0xff, no infinities), the stored value times the layout's k_scale /
+ * v_scale being K / V; the computation after the exact widening to bf16 is the
+ * PKV_BF16 one.  lse is always fp32.  The FP8 cache is the step the pages defer
+ * (RL-Kernel issue #152, section Out of scope).
+ */
+enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 };
 
 enum pkv_status {
   PKV_OK = 0,
@@ -76,7 +84,7 @@ enum pkv_status {
 
 /*
  * Shapes and strides of one call.  All strides are in elements.
- *   dtype               pkv_dtype of q, k/v cache, new K/V and out
+ *   dtype               pkv_dtype (element types of q/out and of the cache/new K/V)
  *   batch               B, number of sequences
  *   num_heads_q         Hq; num_heads_q % num_heads_k == 0
  *   num_heads_k         Hkv
@@ -89,6 +97,10 @@ enum pkv_status {
  *   total_q             rows of q / out / lse (cu_seqlens_q[batch])
  *   num_blocks          blocks in the pool (used only by debug checks)
  *   k_* / v_*_stride    element strides of the K and V caches: block, slot, head
+ *   k_scale, v_scale    K = stored * k_scale, V = stored * v_scale (0 means 1; must be
+ *                       finite and >= 0).  k_scale enters the score multiplier
+ *                       (softmax_scale * k_scale); v_scale multiplies each output once,
+ *                       after the division by the row sum.  The backward requires 1.
  * q and out are packed [total_q, Hq, d]; lse is [total_q, Hq] fp32.
  */
 typedef struct pkv_layout {
@@ -105,6 +117,8 @@ typedef struct pkv_layout {
   int64_t num_blocks;
   int64_t k_block_stride, k_slot_stride, k_head_stride;
   int64_t v_block_stride, v_slot_stride, v_head_stride;
+  float k_scale;
+  float v_scale;
 } pkv_layout;
 
 /*

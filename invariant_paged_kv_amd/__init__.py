@@ -23,7 +23,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL = 1, 2, 3
 CHUNK_KEYS = 512
 TILE_KEYS = 64
@@ -67,6 +67,8 @@ class PkvLayout(ctypes.Structure):
         ("v_block_stride", ctypes.c_int64),
         ("v_slot_stride", ctypes.c_int64),
         ("v_head_stride", ctypes.c_int64),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -126,21 +128,30 @@ def _check(rc: int, where: str) -> None:
 
 
 def _dtype_code(t: torch.dtype) -> int:
+    """pkv_dtype of a cache: its storage type (an FP8 cache goes with bf16 queries)."""
     if t == torch.bfloat16:
         return PKV_BF16
     if t == torch.float32:
         return PKV_F32
+    if t == torch.float8_e4m3fn:
+        return PKV_FP8_E4M3
     raise TypeError(f"unsupported dtype {t}")
+
+
+def query_dtype(cache_dtype: torch.dtype) -> torch.dtype:
+    """Element type of q/out for a cache of ``cache_dtype``."""
+    return torch.bfloat16 if cache_dtype == torch.float8_e4m3fn else cache_dtype
 
 
 def make_layout(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                 num_heads_q: int, max_seqlen_q: int, total_q: int, max_seqlen_k: int = 0,
-                batch: Optional[int] = None) -> PkvLayout:
+                batch: Optional[int] = None, k_scale: float = 1.0, v_scale: float = 1.0) -> PkvLayout:
     """``pkv_layout`` from the cache views' shapes and strides.
 
     ``k_cache``/``v_cache`` are ``[num_blocks, block_size, Hkv, d]`` views with
     unit stride in the last dimension; any block/slot/head strides (e.g. the
-    K/V-interleaved layout) are passed through as they are.
+    K/V-interleaved layout) are passed through as they are.  ``k_scale`` /
+    ``v_scale`` turn stored values into K / V (FP8 caches).
     """
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache must be [num_blocks, block_size, Hkv, d] with equal shapes")
@@ -163,6 +174,8 @@ def make_layout(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch
     L.num_blocks = nb
     L.k_block_stride, L.k_slot_stride, L.k_head_stride = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
     L.v_block_stride, L.v_slot_stride, L.v_head_stride = v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)
+    L.k_scale = float(k_scale)
+    L.v_scale = float(v_scale)
     return L
 
 
@@ -180,7 +193,8 @@ def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  block_table: torch.Tensor, seqlens_k: torch.Tensor, cu_seqlens_q: torch.Tensor,
                  causal: bool, softmax_scale: float, *, max_seqlen_q: int, max_seqlen_k: int = 0,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 workspace: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                 v_scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention of packed queries ``q [total_q, Hq, d]`` against the paged cache.
 
     ``seqlens_k[b]`` keys are visible to sequence ``b`` (including its own new
@@ -191,9 +205,10 @@ def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [total_q, Hq, d] tensor")
-    if q.dtype != k_cache.dtype:
-        raise TypeError("q and cache dtypes differ")
-    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k)
+    if q.dtype != query_dtype(k_cache.dtype):
+        raise TypeError("q dtype does not match the cache (bf16 queries for an FP8 cache)")
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k,
+                      k_scale=k_scale, v_scale=v_scale)
     if lay.head_dim != q.shape[2]:
         raise ValueError("q head_dim differs from the cache's")
     if out is None:
@@ -221,7 +236,8 @@ def attn_forward_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
                         cu_seqlens_q: torch.Tensor, causal: bool, softmax_scale: float, *, max_seqlen_q: int,
                         max_seqlen_k: int = 0, out: Optional[torch.Tensor] = None,
                         lse: Optional[torch.Tensor] = None,
-                        workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                        workspace: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                        v_scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Write ``k_new``/``v_new`` (one row per query row, at the row's own key
     position ``seqlens_k[b] - L + r``) into the cache and attend, in one launch.
 
@@ -233,7 +249,10 @@ def attn_forward_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
     for t, name in ((k_new, "k_new"), (v_new, "v_new")):
         if t.dim() != 3 or not t.is_contiguous() or t.dtype != k_cache.dtype or t.shape[0] != q.shape[0]:
             raise ValueError(f"{name} must be a contiguous [total_q, Hkv, d] tensor of the cache dtype")
-    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k)
+    if q.dtype != query_dtype(k_cache.dtype):
+        raise TypeError("q dtype does not match the cache (bf16 queries for an FP8 cache)")
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k,
+                      k_scale=k_scale, v_scale=v_scale)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:

@@ -41,7 +41,20 @@ int ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int elem_bytes(int dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+// Bytes per element of the cache / new K/V rows, and of q / out.
+int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 1; }
+int q_elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+// Stored-value scales: 0 means 1.
+float kv_scale(float s) { return s == 0.f ? 1.f : s; }
+
+// Score multiplier: softmax_scale * k_scale, times log2(e) for the base-2
+// (bf16-computing) types; one rounding, from double.
+float score_mul(const pkv_layout& l, float softmax_scale) {
+  double m = static_cast<double>(softmax_scale) * static_cast<double>(kv_scale(l.k_scale));
+  if (l.dtype != PKV_F32) m *= 1.4426950408889634074;
+  return static_cast<float>(m);
+}
 
 int64_t max_seqlen_k_of(const pkv_layout& l) {
   const int64_t cap = static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size;
@@ -50,7 +63,10 @@ int64_t max_seqlen_k_of(const pkv_layout& l) {
 
 int validate(const pkv_layout* l) {
   if (!l) return fail(PKV_ERR_NULL, "kv_strides (layout) is NULL");
-  if (l->dtype != PKV_F32 && l->dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "dtype %d is not PKV_F32 or PKV_BF16", l->dtype);
+  if (l->dtype != PKV_F32 && l->dtype != PKV_BF16 && l->dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_DTYPE, "dtype %d is not PKV_F32, PKV_BF16 or PKV_FP8_E4M3", l->dtype);
+  if (!std::isfinite(l->k_scale) || !std::isfinite(l->v_scale) || l->k_scale < 0.f || l->v_scale < 0.f)
+    return fail(PKV_ERR_SHAPE, "k_scale and v_scale must be finite and >= 0 (0 means 1)");
   if (l->batch < 0) return fail(PKV_ERR_SHAPE, "batch %d < 0", l->batch);
   if (l->num_heads_k < 1 || l->num_heads_q < 1 || l->num_heads_q % l->num_heads_k != 0)
     return fail(PKV_ERR_SHAPE, "num_heads_q %d must be a positive multiple of num_heads_k %d", l->num_heads_q, l->num_heads_k);
@@ -198,8 +214,8 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.maxc = p.maxc;
   a.cpi = p.cpi;
   a.causal = causal ? 1 : 0;
-  a.mul = l->dtype == PKV_BF16 ? static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634074)
-                               : softmax_scale;
+  a.mul = score_mul(*l, softmax_scale);
+  a.v_scale = kv_scale(l->v_scale);
   pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
   a.k_new = k_new;
   a.v_new = v_new;
@@ -225,6 +241,9 @@ int run_backward(const void* q, const void* k_cache, const void* v_cache, const 
                  hipStream_t stream) {
   int rc = validate(l);
   if (rc) return rc;
+  if (l->dtype == PKV_FP8_E4M3) return fail(PKV_ERR_DTYPE, "the backward takes PKV_F32 or PKV_BF16 caches");
+  if (kv_scale(l->k_scale) != 1.f || kv_scale(l->v_scale) != 1.f)
+    return fail(PKV_ERR_SHAPE, "the backward requires k_scale = v_scale = 1");
   rc = check_attn_ptrs(q, k_cache, v_cache, block_table, seqlens_k, cu_seqlens_q, out, lse, *l);
   if (rc) return rc;
   if (total_k < 0) return fail(PKV_ERR_SHAPE, "total_k %lld < 0", (long long)total_k);
@@ -271,8 +290,8 @@ int run_backward(const void* q, const void* k_cache, const void* v_cache, const 
   a.mbps = l->max_blocks_per_seq;
   a.ncb = static_cast<int>((cols + 16 * kWaves - 1) / (16 * kWaves));
   a.causal = causal ? 1 : 0;
-  a.mul = l->dtype == PKV_BF16 ? static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634074)
-                               : softmax_scale;
+  a.mul = score_mul(*l, softmax_scale);
+  a.v_scale = kv_scale(l->v_scale);
   pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
   b.cu_k = cu_seqlens_k;
   b.out = out;

@@ -23,13 +23,14 @@
 namespace pkv {
 
 template <class T, int D>
-__device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (&o)[D / 16], float M, float Ls) {
+__device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (&o)[D / 16], float M, float Ls,
+                                          float vs) {
   const int G = lane_id() >> 4;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
     const int e = 16 * dt + 4 * G;
-    float v0 = final_val(M, o[dt][0], Ls), v1 = final_val(M, o[dt][1], Ls);
-    float v2 = final_val(M, o[dt][2], Ls), v3 = final_val(M, o[dt][3], Ls);
+    float v0 = final_val(M, o[dt][0], Ls, vs), v1 = final_val(M, o[dt][1], Ls, vs);
+    float v2 = final_val(M, o[dt][2], Ls, vs), v3 = final_val(M, o[dt][3], Ls, vs);
     if constexpr (T::EB == 2) {
       u32x2 w = {bf16_rne_bits(v0) | (bf16_rne_bits(v1) << 16), bf16_rne_bits(v2) | (bf16_rne_bits(v3) << 16)};
       *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + elem + e) = w;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
       if (col < ncols) {
         const int64_t rh = (int64_t)(q0 + col / g) * a.hq + hk * g + col % g;
         if (G == 0) a.lse[rh] = final_lse<T>(M[nt], Ls[nt]);
-        store_out<T, D>(a.out, rh * D, O[nt], M[nt], Ls[nt]);
+        store_out<T, D>(a.out, rh * D, O[nt], M[nt], Ls[nt], a.v_scale);
       }
     }
   }
@@ -185,9 +186,32 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <class T, int D>
 struct TileRegs {
-  KOps<T, D> k;
-  KOps<T, D> v;
+  using Raw = typename KvRaw<T>::type;  // stored bytes; widened where they are used
+  Raw k[KT / 16][TileGeom<T, D>::NK];
+  Raw v[KT / 16][TileGeom<T, D>::NK];
 };
+
+// QK^T of a tile whose K operands are held as stored bytes: the qk_tile chain,
+// each operand widened just before its MFMA.
+template <class T, int D>
+__device__ __forceinline__ void qk_tile_regs(const TileRegs<T, D>& r, const QOps<T, D>& q, f32x4 (&s)[KT / 16]) {
+  using G_ = TileGeom<T, D>;
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) {
+      const u32x4 kw = kv_widen<T>(r.k[mt][k]);
+      if constexpr (T::EB == 2) {
+        acc = mfma_bf16(kw, q.v[k], acc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(__uint_as_float(kw[e]), __uint_as_float(q.v[k][e]), acc);
+      }
+    }
+    s[mt] = acc;
+  }
+}
 
 // Block ids of this lane's four tile rows (rows past jlast use the last
 // visible row's block, so every read stays inside the sequence's blocks).
@@ -215,22 +239,25 @@ __device__ __forceinline__ void tile_load_regs(const AttnArgs& a, int hk, int j0
     const int jc = min(j, jlast - 1);  // rows past jlast load a visible row, then read as zero
     const int64_t blk = ids[mt];
     const int64_t slot = jc - div_block(jc, a.bs_mul, a.bs_shift) * a.bs;
-    const unsigned char* kp = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::EB + 16 * (lane >> 4);
-    const unsigned char* vp = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::EB + 16 * (lane >> 4);
+    constexpr int P = kKvPiece<T>;  // stored bytes per 16-byte operand piece
+    const int off = P * (lane >> 4);
+    const unsigned char* kp = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::KVB + off;
+    const unsigned char* vp = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::KVB + off;
     const int nhk = a.hq / a.g;
-    const unsigned char* ks = kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kp, 16 * (lane >> 4));
-    const unsigned char* vs = kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vp, 16 * (lane >> 4));
+    const unsigned char* ks = kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kp, off);
+    const unsigned char* vs = kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vp, off);
+    using Raw = typename KvRaw<T>::type;
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) {
       if (want_k) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(ks + 64 * k);
-        kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kp + 64 * k, x);
-        r.k[mt][k] = in ? x : u32x4{0, 0, 0, 0};
+        const Raw x = kv_load_raw<T>(ks + 4 * P * k);
+        kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kp + 4 * P * k, x);
+        r.k[mt][k] = in ? x : Raw{};
       }
       if (want_v) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vs + 64 * k);
-        kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vp + 64 * k, x);
-        r.v[mt][k] = in ? x : u32x4{0, 0, 0, 0};
+        const Raw x = kv_load_raw<T>(vs + 4 * P * k);
+        kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vp + 4 * P * k, x);
+        r.v[mt][k] = in ? x : Raw{};
       }
     }
   }
@@ -244,7 +271,8 @@ __device__ __forceinline__ void tile_store_v(unsigned char* v_lds, const TileReg
 #pragma unroll
   for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
-    for (int k = 0; k < G_::NK; ++k) *reinterpret_cast<u32x4*>(base + mt * 16 * G_::VPITCH + 64 * k) = r.v[mt][k];
+    for (int k = 0; k < G_::NK; ++k)
+      *reinterpret_cast<u32x4*>(base + mt * 16 * G_::VPITCH + 64 * k) = kv_widen<T>(r.v[mt][k]);
 }
 
 #ifndef PKV_PF_XCD
@@ -263,8 +291,8 @@ template <class T, int D, int W>
 struct PrefillStage {
   static constexpr int NCH = KT * TileGeom<T, D>::CPR;  // 16-byte pieces per tensor per tile
   static constexpr int PER = NCH / (64 * W);
-  u32x4 k[PER];
-  u32x4 v[PER];
+  typename KvRaw<T>::type k[PER];  // stored bytes, widened when written to LDS
+  typename KvRaw<T>::type v[PER];
 };
 
 template <class T, int D, int W, bool APPEND>
@@ -284,16 +312,17 @@ __device__ __forceinline__ void prefill_load(const AttnArgs& a, const int32_t* b
     const int bi = div_block(jc, a.bs_mul, a.bs_shift);
     const int64_t blk = bt[bi];
     const int64_t slot = jc - bi * a.bs;
-    const unsigned char* kc = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::EB + 16 * part;
-    const unsigned char* vc = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::EB + 16 * part;
+    const int off = kKvPiece<T> * part;
+    const unsigned char* kc = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::KVB + off;
+    const unsigned char* vc = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::KVB + off;
     const int nhk = a.hq / a.g;
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, 16 * part));
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, 16 * part));
+    const auto kv = kv_load_raw<T>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, off));
+    const auto vv = kv_load_raw<T>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, off));
     const bool in = j < jmax;
     kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kc, kv);
     kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vc, vv);
-    r.k[i] = in ? kv : u32x4{0, 0, 0, 0};
-    r.v[i] = in ? vv : u32x4{0, 0, 0, 0};
+    r.k[i] = in ? kv : typename KvRaw<T>::type{};
+    r.v[i] = in ? vv : typename KvRaw<T>::type{};
   }
 }
 
@@ -305,8 +334,8 @@ __device__ __forceinline__ void prefill_store(unsigned char* k_lds, unsigned cha
   for (int i = 0; i < S_::PER; ++i) {
     const int qi = threadIdx.x + i * 64 * W;
     const int row = qi / G_::CPR, part = qi % G_::CPR;
-    *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = r.k[i];
-    *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = r.v[i];
+    *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = kv_widen<T>(r.k[i]);
+    *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = kv_widen<T>(r.v[i]);
   }
 }
 
@@ -424,7 +453,7 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
   if (col < ncols) {
     const int64_t rh = (int64_t)(q0 + col / g) * a.hq + hk * g + col % g;
     if (G == 0) a.lse[rh] = final_lse<T>(M, Ls);
-    store_out<T, D>(a.out, rh * D, O, M, Ls);
+    store_out<T, D>(a.out, rh * D, O, M, Ls, a.v_scale);
   }
 }
 
@@ -494,7 +523,7 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
       tile_store_v<T, D>(v_lds, r);
       if (more) tile_load_regs<T, D, APPEND>(a, hk, jn, jlast, ids, r, false, true, ap);
       f32x4 s[1][KT / 16];
-      qk_tile<T, D>(r.k, q, s[0]);
+      qk_tile_regs<T, D>(r, q, s[0]);
       if (more) {
         tile_load_regs<T, D, APPEND>(a, hk, jn, jlast, ids, r, true, false, ap);
         tile_block_ids(a, bt, jn + KT, jlast, ids);
@@ -577,11 +606,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if constexpr (T::EB == 2) {
     uint16_t* o = static_cast<uint16_t*>(a.out) + w * D + e0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = static_cast<uint16_t>(bf16_rne_bits(final_val(M, O[e], Ls)));
+    for (int e = 0; e < EPL; ++e) o[e] = static_cast<uint16_t>(bf16_rne_bits(final_val(M, O[e], Ls, a.v_scale)));
   } else {
     float* o = static_cast<float*>(a.out) + w * D + e0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = final_val(M, O[e], Ls);
+    for (int e = 0; e < EPL; ++e) o[e] = final_val(M, O[e], Ls, a.v_scale);
   }
 }
 
@@ -627,6 +656,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   m.hq = a.hq;
   m.maxc = a.maxc;
   m.causal = a.causal;
+  m.v_scale = a.v_scale;
   const int64_t waves = pl.total_q * a.hq;
   if (waves == 0) return hipSuccess;
   dim3 mgrid(static_cast<unsigned>((waves * kMergeWavesPerRow + 3) / 4));
@@ -638,6 +668,9 @@ template <bool APPEND>
 static hipError_t launch_attention_t(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream) {
   if (dtype == 1) {
     return d == 128 ? launch_attn_t<TBf16, 128, APPEND>(a, pl, stream) : launch_attn_t<TBf16, 64, APPEND>(a, pl, stream);
+  }
+  if (dtype == 2) {
+    return d == 128 ? launch_attn_t<TFp8, 128, APPEND>(a, pl, stream) : launch_attn_t<TFp8, 64, APPEND>(a, pl, stream);
   }
   return d == 128 ? launch_attn_t<TF32, 128, APPEND>(a, pl, stream) : launch_attn_t<TF32, 64, APPEND>(a, pl, stream);
 }

@@ -33,9 +33,10 @@
 namespace pkv {
 
 // Natural-log LSE in the score units of T (bf16 scores are in base 2).
-template <class T> __device__ __forceinline__ float lse_units(float lse);
-template <> __device__ __forceinline__ float lse_units<TBf16>(float lse) { return lse * 1.44269504088896340736f; }
-template <> __device__ __forceinline__ float lse_units<TF32>(float lse) { return lse; }
+template <class T> __device__ __forceinline__ float lse_units(float lse) {
+  if constexpr (T::kBase2) return lse * 1.44269504088896340736f;
+  else return lse;
+}
 
 __device__ __forceinline__ float elem_f32(const void* p, int64_t i, int eb) {
   if (eb == 2) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);

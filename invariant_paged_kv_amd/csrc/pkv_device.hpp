@@ -40,19 +40,32 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // softmax (scores pre-multiplied by scale*log2(e), exp2 via v_exp_f32).
 // TF32: fp32 storage, MFMA 16x16x4 fp32, natural-base expf/logf (the fp32
 // tolerances leave no room for the base-2 rewrite's extra rounding).
+// TFp8: bf16 queries and outputs, K/V cache stored as OCP FP8 E4M3 bytes;
+// the loaders widen each byte exactly to bf16, so everything after the load is
+// the TBf16 computation (the per-tensor K/V scales are applied to the score
+// multiplier and to the final output).
+// EB: bytes per query/output element; KVB: bytes per stored K/V element.
 // ---------------------------------------------------------------------------
 struct TBf16 {
-  static constexpr int EB = 2;  // bytes per element
+  static constexpr int EB = 2;
+  static constexpr int KVB = 2;
   static constexpr bool kBase2 = true;
 };
 struct TF32 {
   static constexpr int EB = 4;
+  static constexpr int KVB = 4;
   static constexpr bool kBase2 = false;
 };
+struct TFp8 {
+  static constexpr int EB = 2;
+  static constexpr int KVB = 1;
+  static constexpr bool kBase2 = true;
+};
 
-template <class T> __device__ __forceinline__ float pkv_exp(float x);
-template <> __device__ __forceinline__ float pkv_exp<TBf16>(float x) { return __builtin_amdgcn_exp2f(x); }
-template <> __device__ __forceinline__ float pkv_exp<TF32>(float x) { return expf(x); }
+template <class T> __device__ __forceinline__ float pkv_exp(float x) {
+  if constexpr (T::kBase2) return __builtin_amdgcn_exp2f(x);
+  else return expf(x);
+}
 
 // How far a column's tile max may exceed its reference max before the
 // reference moves (and o, l are rescaled): 8 score units, so p <= 2^8 (bf16,
@@ -60,11 +73,38 @@ template <> __device__ __forceinline__ float pkv_exp<TF32>(float x) { return exp
 template <class T> constexpr float kRescaleSlack = 8.0f;
 
 // Natural-log LSE from the running max m and sum l (m in the score units of T).
-template <class T> __device__ __forceinline__ float pkv_lse(float m, float l);
-template <> __device__ __forceinline__ float pkv_lse<TBf16>(float m, float l) {
-  return (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;  // v_log_f32 is log2
+template <class T> __device__ __forceinline__ float pkv_lse(float m, float l) {
+  if constexpr (T::kBase2) return (m + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;  // v_log_f32 is log2
+  else return m + logf(l);
 }
-template <> __device__ __forceinline__ float pkv_lse<TF32>(float m, float l) { return m + logf(l); }
+
+// Stored K/V bytes that feed one 16-byte (compute-type) operand piece: 16
+// bytes for bf16/fp32 caches, 8 FP8 bytes for 8 bf16 elements.
+template <class T> struct KvRaw { using type = u32x4; };
+template <> struct KvRaw<TFp8> { using type = u32x2; };
+template <class T> constexpr int kKvPiece = 16 * T::KVB / T::EB;
+
+// Widen stored K/V bytes to the compute type.  FP8 E4M3 -> bf16 is exact
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3 value, subnormals
+// included, is a bf16 value); element e of the piece is byte e.
+template <class T>
+__device__ __forceinline__ u32x4 kv_widen(const typename KvRaw<T>::type& r) {
+  if constexpr (T::KVB == T::EB) {
+    return r;
+  } else {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[0], 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[0], 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, true);
+    return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                 __builtin_bit_cast(uint32_t, d)};
+  }
+}
+
+template <class T>
+__device__ __forceinline__ typename KvRaw<T>::type kv_load_raw(const unsigned char* p) {
+  return *reinterpret_cast<const typename KvRaw<T>::type*>(p);
+}
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN).  Result in the low 16 bits.
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -392,6 +432,9 @@ template <class T>
 __device__ __forceinline__ float final_lse(float M, float L) {
   return M == -INFINITY ? -INFINITY : pkv_lse<T>(M, L);
 }
-__device__ __forceinline__ float final_val(float M, float O, float L) { return M == -INFINITY ? 0.f : O / L; }
+// vs: the stored-V scale (1 for unscaled caches: the multiply is then exact).
+__device__ __forceinline__ float final_val(float M, float O, float L, float vs) {
+  return M == -INFINITY ? 0.f : (O / L) * vs;
+}
 
 }  // namespace pkv

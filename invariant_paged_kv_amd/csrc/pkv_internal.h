@@ -25,7 +25,8 @@ struct AttnArgs {
   int32_t maxc;    // chunk capacity of the partial buffers
   int32_t cpi;     // chunks per split work item
   int32_t causal;
-  float mul;       // score multiplier: scale (fp32) or scale*log2(e) (bf16)
+  float mul;       // score multiplier: scale * k_scale (fp32), times log2(e) for base-2 types
+  float v_scale;   // stored-V scale, applied at the final write (1: unscaled)
   uint32_t bs_mul; // j / bs == (j * bs_mul) >> bs_shift for 0 <= j < 2^30
   int32_t bs_shift;
   // Fused append (pkv_attn_forward_append): the K/V rows of this call's query
@@ -47,6 +48,7 @@ struct MergeArgs {
   float* lse;
   int64_t total_q;
   int32_t batch, hq, maxc, causal;
+  float v_scale;
 };
 
 struct LaunchPlan {

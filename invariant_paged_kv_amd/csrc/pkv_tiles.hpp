@@ -30,14 +30,15 @@ __device__ __forceinline__ Append make_append(int n, int L, int q0, bool last_bl
   return ap;
 }
 
-// Address of the 16-byte piece `byte_off` of key row jc (cache address
-// `cache`), redirected to the caller's new rows under fused append.
+// Address of the stored piece at byte `byte_off` of key row jc (cache address
+// `cache`), redirected to the caller's new rows under fused append (the new
+// rows are in the cache's storage type).
 template <class T, int D, bool APPEND>
 __device__ __forceinline__ const unsigned char* kv_src(const void* new_base, int nhk, int hk, int jc,
                                                         const Append& ap, const unsigned char* cache, int byte_off) {
   if constexpr (APPEND) {
     const int64_t nrow = (ap.row0 + (jc - ap.n_old)) * nhk + hk;
-    const unsigned char* np = static_cast<const unsigned char*>(new_base) + nrow * D * T::EB + byte_off;
+    const unsigned char* np = static_cast<const unsigned char*>(new_base) + nrow * D * T::KVB + byte_off;
     return jc >= ap.n_old ? np : cache;
   } else {
     return cache;
@@ -46,19 +47,20 @@ __device__ __forceinline__ const unsigned char* kv_src(const void* new_base, int
 
 template <class T, bool APPEND>
 __device__ __forceinline__ void kv_store_new(const Append& ap, bool in, int jc, void* store_base, const void* load_base,
-                                             const unsigned char* cache, u32x4 x) {
+                                             const unsigned char* cache, const typename KvRaw<T>::type& x) {
   if constexpr (APPEND) {
     if (ap.writer && in && jc >= ap.n_old) {
       unsigned char* dst = static_cast<unsigned char*>(store_base) + (cache - static_cast<const unsigned char*>(load_base));
-      *reinterpret_cast<u32x4*>(dst) = x;
+      *reinterpret_cast<typename KvRaw<T>::type*>(dst) = x;
     }
   }
 }
 
-// K/V tile loader: keys j0 .. j0+KT-1 of one sequence and KV head into LDS,
-// 16-byte loads, consecutive lanes on consecutive 16 bytes of a key row.  The
-// block address uses the real block stride (contiguous or K/V-interleaved
-// caches alike).  Keys >= jmax are not read; their rows are zero.
+// K/V tile loader: keys j0 .. j0+KT-1 of one sequence and KV head into LDS
+// (in the compute type), consecutive lanes on consecutive 16-byte pieces of a
+// key row (16 stored bytes, or 8 FP8 bytes widened to 16).  The block address
+// uses the real block stride (contiguous or K/V-interleaved caches alike).
+// Keys >= jmax are not read; their rows are zero.
 template <class T, int D, int W, bool APPEND>
 __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
                                           unsigned char* k_lds, unsigned char* v_lds, const Append& ap) {
@@ -81,16 +83,17 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
       const int bi = div_block(jc, a.bs_mul, a.bs_shift);
       const int64_t blk = bt[bi];
       const int64_t slot = jc - bi * a.bs;
-      const unsigned char* kc = kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::EB + 16 * part;
-      const unsigned char* vc = vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::EB + 16 * part;
+      const int off = kKvPiece<T> * part;
+      const unsigned char* kc = kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::KVB + off;
+      const unsigned char* vc = vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::KVB + off;
       const int nhk = a.hq / a.g;
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, 16 * part));
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, 16 * part));
+      const auto kv = kv_load_raw<T>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, off));
+      const auto vv = kv_load_raw<T>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, off));
       const bool in = j < jmax;
       kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kc, kv);
       kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vc, vv);
-      kr[i] = in ? kv : u32x4{0, 0, 0, 0};
-      vr[i] = in ? vv : u32x4{0, 0, 0, 0};
+      kr[i] = in ? kv_widen<T>(kv) : u32x4{0, 0, 0, 0};
+      vr[i] = in ? kv_widen<T>(vv) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {

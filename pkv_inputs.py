@@ -93,13 +93,15 @@ def relayout(pool: PagedKV, layout: str) -> PagedKV:
     """The same K/V values in another layout (a pure copy)."""
     nb, bs, hk, d = pool.k.shape
     dt = pool.k.dtype
+    # copy FP8 as raw bytes (byte views copy on every device)
+    raw = (lambda t: t.view(torch.uint8)) if dt == torch.float8_e4m3fn else (lambda t: t)
     if layout == "interleaved":
         buf = torch.empty((nb, 2, bs, hk, d), dtype=dt, device=pool.k.device)
-        buf[:, 0].copy_(pool.k)
-        buf[:, 1].copy_(pool.v)
+        raw(buf)[:, 0].copy_(raw(pool.k))
+        raw(buf)[:, 1].copy_(raw(pool.v))
         return PagedKV(buf[:, 0], buf[:, 1], layout, [buf])
-    k = pool.k.contiguous().clone()
-    v = pool.v.contiguous().clone()
+    k = raw(pool.k).contiguous().clone().view(dt)
+    v = raw(pool.v).contiguous().clone().view(dt)
     return PagedKV(k, v, "contiguous", [k, v])
 
 

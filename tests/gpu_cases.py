@@ -103,12 +103,15 @@ def subset_for_oracle(case: Case, seq_ids: Sequence[int]):
     ks, vs, rows, tables, seqlens, cu = [], [], [], [], [], [0]
     nxt = 0
     maxblk = max(max(1, (case.seqlens[b] + bs - 1) // bs) for b in seq_ids)
+    fp8 = case.pool.k.dtype == torch.float8_e4m3fn
+    kview = case.pool.k.view(torch.uint8) if fp8 else case.pool.k   # byte view: index FP8 as raw bytes
+    vview = case.pool.v.view(torch.uint8) if fp8 else case.pool.v
     for b in seq_ids:
         n = case.seqlens[b]
         nblk = (n + bs - 1) // bs
         ids = bt[b, :nblk].long().to(DEV)
-        ks.append(case.pool.k.index_select(0, ids).cpu())
-        vs.append(case.pool.v.index_select(0, ids).cpu())
+        ks.append(kview.index_select(0, ids).cpu())
+        vs.append(vview.index_select(0, ids).cpu())
         row = list(range(nxt, nxt + nblk)) + [0] * (maxblk - nblk)
         tables.append(row)
         nxt += nblk
@@ -116,8 +119,10 @@ def subset_for_oracle(case: Case, seq_ids: Sequence[int]):
         rows.extend(range(r0, r1))
         seqlens.append(n)
         cu.append(cu[-1] + r1 - r0)
-    k = torch.cat(ks) if nxt else torch.zeros((1,) + tuple(case.pool.k.shape[1:]), dtype=case.pool.k.dtype)
+    k = torch.cat(ks) if nxt else torch.zeros((1,) + tuple(kview.shape[1:]), dtype=kview.dtype)
     v = torch.cat(vs) if nxt else torch.zeros_like(k)
+    if fp8:
+        k, v = k.view(torch.float8_e4m3fn), v.view(torch.float8_e4m3fn)
     if nxt == 0:
         tables = [[0] * maxblk for _ in seq_ids]
     pool = gen.PagedKV(k.contiguous(), v.contiguous(), "contiguous", [])

@@ -21,7 +21,7 @@ def declared_functions():
 def test_library_is_built_and_loads():
     assert os.path.exists(pkv.LIB_PATH), "run python -m invariant_paged_kv_amd.build"
     L = pkv.lib()
-    assert L.pkv_abi_version() == 1
+    assert L.pkv_abi_version() == 2
 
 
 def test_exports_every_declared_symbol():
@@ -56,6 +56,12 @@ def good_layout(**over):
     ({"dtype": pkv.PKV_F32, "k_head_stride": 132}, 0),
     ({"dtype": pkv.PKV_F32, "k_head_stride": 130}, -4),
     ({"max_seqlen_q": -1}, -2),
+    ({"dtype": pkv.PKV_FP8_E4M3}, 0),
+    ({"dtype": pkv.PKV_FP8_E4M3, "k_slot_stride": 4 * 128 + 8}, -4),   # 8 bytes: not a 16-byte multiple
+    ({"dtype": 3}, -3),
+    ({"k_scale": -1.0}, -2),
+    ({"v_scale": float("nan")}, -2),
+    ({"k_scale": 0.5, "v_scale": 0.0}, 0),
 ])
 def test_validate_layout(over, code):
     L = pkv.lib()
@@ -124,6 +130,24 @@ def test_backward_rejects_bad_arguments_before_launch():
     rc = L.pkv_attn_backward(16, 16, 32, ctypes.byref(lay), 64, 64, 64, 64, 10, 1, 0.1, 48, 64, 80, 96, 112, 128,
                              256, 4, None)
     assert rc == -5
+
+
+def test_backward_rejects_fp8_and_scaled_caches():
+    L = pkv.lib()
+    for over, code in (({"dtype": pkv.PKV_FP8_E4M3}, -3), ({"k_scale": 2.0}, -2), ({"v_scale": 0.5}, -2)):
+        lay = good_layout(total_q=2, **over)
+        rc = L.pkv_attn_backward(16, 16, 32, ctypes.byref(lay), 64, 64, 64, 64, 10, 1, 0.1, 48, 64, 80, 96, 112,
+                                 128, None, 0, None)
+        assert rc == code, (over, rc)
+
+
+def test_layout_struct_matches_header():
+    """The ctypes mirror has the header's fields, in order, at the C offsets."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct pkv_layout \{(.*?)\} pkv_layout;", text, re.S).group(1)
+    names = re.findall(r"(\w+)\s*[,;]", body)
+    assert [f[0] for f in pkv.PkvLayout._fields_] == names
+    assert ctypes.sizeof(pkv.PkvLayout) == 8 * 4 + 9 * 8 + 2 * 4   # no padding: 112 bytes
 
 
 def test_backward_workspace_size():
