@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--seqlen-k", type=int, default=131072)
     return ap.parse_args()
@@ -168,6 +169,8 @@ def main():
     }
     del ws, p_out, p_lse
 
+    if not args.no_fp8:
+        result["fp8_decode"] = bench_fp8_decode(torch, pkv, gen, B, N, args.steps, args.warmup, attn_avg_ms)
     if not args.no_prefill:
         result["prefill"], result["backward"] = bench_prefill(torch, pkv, gen)
     if not args.no_cpu_baseline:
@@ -196,6 +199,58 @@ def measured_traffic():
     if h.hexdigest() != info.get("source_sha256"):
         return None
     return info.get("traffic_bytes_per_launch")
+
+
+def bench_fp8_decode(torch, pkv, gen, B, N, steps, warmup, bf16_ms):
+    """The same decode call over an FP8 E4M3 cache of the same shape (half the KV bytes)."""
+    dev = "cuda"
+    HQ, HK, D, BS = 64, 8, 128, 256
+    nb = gen.pool_num_blocks(N, BS, B)
+    g = torch.Generator(device=dev).manual_seed(1006)
+    pool = gen.new_pool(nb, BS, HK, D, "fp8", "interleaved", device=dev, generator=g)
+    bt = gen.randperm_block_table(nb, B, generator=torch.Generator().manual_seed(1006)).to(dev)
+    q = gen.randn((B, HQ, D), "bf16", generator=g, device=dev)
+    seqlens = torch.full((B,), N, dtype=torch.int32, device=dev)
+    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    scale, ks, vs = 1.0 / math.sqrt(D), 0.5, 1.25
+    out = torch.empty_like(q)
+    lse = torch.empty((B, HQ), dtype=torch.float32, device=dev)
+    ws = torch.empty(pkv.workspace_size(q, pool.k, pool.v, bt, max_seqlen_q=1, max_seqlen_k=N), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+
+    def call():
+        ev0.record(stream)
+        pkv.attn_forward(q, pool.k, pool.v, bt, seqlens, cu, True, scale, max_seqlen_q=1, max_seqlen_k=N, out=out,
+                         lse=lse, workspace=ws, k_scale=ks, v_scale=vs)
+        ev1.record(stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    total = 0.0
+    for _ in range(steps):
+        call()
+        ev1.synchronize()
+        total += ev0.elapsed_time(ev1)
+    ms = total / steps
+    with pkv.options(path=2):
+        p_out, p_lse = pkv.attn_forward(q, pool.k, pool.v, bt, seqlens, cu, True, scale, max_seqlen_q=1,
+                                        max_seqlen_k=N, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(p_out.view(torch.int16), out.view(torch.int16))
+                and torch.equal(p_lse.view(torch.int32), lse.view(torch.int32)))
+    kv_bytes = B * N * HK * D * 1 * 2
+    call_bytes = kv_bytes + 2 * q.numel() * 2 + lse.numel() * 4 + B * math.ceil(N / BS) * 4 + 2 * (B + 1) * 4
+    gbs = call_bytes / (ms * 1e-3) / 1e9
+    del pool, ws, p_out, p_lse
+    torch.cuda.empty_cache()
+    return {"workload": "the decode call over an FP8 E4M3 cache of the same shape (k_scale 0.5, v_scale 1.25)",
+            "avg_ms": round(ms, 4), "bytes_per_launch": call_bytes, "achieved_GBs": round(gbs, 2),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "keys_per_s": round(B * N / (ms * 1e-3), 1),
+            "speedup_vs_bf16_call": round(bf16_ms / ms, 3), "bitwise_decode_eq_prefill_kernel": same}
 
 
 def bench_prefill(torch, pkv, gen, reps: int = 3):

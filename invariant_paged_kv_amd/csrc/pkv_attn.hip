@@ -89,9 +89,9 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
     lim[nt] = column_limit(col, ncols, g, n, L, a.causal);
     if (col < ncols) {
       const int64_t qelem = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * D;
-      const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB + 16 * G;
+      const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB;
 #pragma unroll
-      for (int k = 0; k < G_::NK; ++k) q[nt].v[k] = *reinterpret_cast<const u32x4*>(qp + 64 * k);
+      for (int k = 0; k < G_::NK; ++k) q[nt].v[k] = *reinterpret_cast<const u32x4*>(qp + qk_piece_off<T>(k, G));
     } else {
 #pragma unroll
       for (int k = 0; k < G_::NK; ++k) q[nt].v[k] = u32x4{0, 0, 0, 0};
@@ -247,6 +247,30 @@ __device__ __forceinline__ void tile_load_regs(const AttnArgs& a, int hk, int j0
     const unsigned char* ks = kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kp, off);
     const unsigned char* vs = kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vp, off);
     using Raw = typename KvRaw<T>::type;
+    if constexpr (T::KVB == 1) {
+      // FP8: pieces k = 2j and 2j+1 of this lane are 16 contiguous stored bytes
+      // at 64j + 16G (the FP8 k-slot map of qk_piece_off).
+      const unsigned char* ks2 = ks - off + 16 * (lane >> 4);
+      const unsigned char* vs2 = vs - off + 16 * (lane >> 4);
+      const unsigned char* kp2 = kp - off + 16 * (lane >> 4);
+      const unsigned char* vp2 = vp - off + 16 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < G_::NK / 2; ++j) {
+        if (want_k) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(ks2 + 64 * j);
+          kv_store_new<TBf16, APPEND>(ap, in, jc, a.k_store, a.k, kp2 + 64 * j, x);
+          r.k[mt][2 * j] = in ? u32x2{x[0], x[1]} : Raw{};
+          r.k[mt][2 * j + 1] = in ? u32x2{x[2], x[3]} : Raw{};
+        }
+        if (want_v) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(vs2 + 64 * j);
+          kv_store_new<TBf16, APPEND>(ap, in, jc, a.v_store, a.v, vp2 + 64 * j, x);
+          r.v[mt][2 * j] = in ? u32x2{x[0], x[1]} : Raw{};
+          r.v[mt][2 * j + 1] = in ? u32x2{x[2], x[3]} : Raw{};
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) {
       if (want_k) {
@@ -267,12 +291,12 @@ template <class T, int D>
 __device__ __forceinline__ void tile_store_v(unsigned char* v_lds, const TileRegs<T, D>& r) {
   using G_ = TileGeom<T, D>;
   const int lane = lane_id();
-  unsigned char* base = v_lds + (lane & 15) * G_::VPITCH + 16 * (lane >> 4);
+  unsigned char* base = v_lds + (lane & 15) * G_::VPITCH;
 #pragma unroll
   for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k)
-      *reinterpret_cast<u32x4*>(base + mt * 16 * G_::VPITCH + 64 * k) = kv_widen<T>(r.v[mt][k]);
+      *reinterpret_cast<u32x4*>(base + mt * 16 * G_::VPITCH + qk_piece_off<T>(k, lane >> 4)) = kv_widen<T>(r.v[mt][k]);
 }
 
 #ifndef PKV_PF_XCD
@@ -417,9 +441,9 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
   QOps<T, D> q;
   if (col < ncols) {
     const int64_t qelem = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * D;
-    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB + 16 * G;
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB;
 #pragma unroll
-    for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + 64 * k);
+    for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + qk_piece_off<T>(k, G));
   } else {
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) q.v[k] = u32x4{0, 0, 0, 0};
@@ -495,9 +519,9 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   QOps<T, D> q;
   if (col < ncols) {
     const int64_t qelem = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * D;
-    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB + 16 * G;
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB;
 #pragma unroll
-    for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + 64 * k);
+    for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + qk_piece_off<T>(k, G));
   } else {
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) q.v[k] = u32x4{0, 0, 0, 0};
@@ -541,6 +565,107 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * G) = st.o[0][dt];
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode split kernel for FP8 caches: stored tiles are half the bytes, so two
+// tiles are kept in flight (register stages ra, rb: tile t is computed from
+// one while the other holds tile t+1, and the consumed one is refilled with
+// tile t+2) -- the same 32 KiB of HBM reads per wave as the bf16 kernel with
+// one tile ahead.  Same chunk core and partial writes as decode_kernel.
+// ---------------------------------------------------------------------------
+template <class T, int D, bool APPEND>
+__device__ __forceinline__ void decode2_tile(const AttnArgs& a, const int32_t* bt, int hk, int t, int t_end, int jlast,
+                                             int (&ids)[KT / 16], TileRegs<T, D>& r, unsigned char* v_lds,
+                                             const QOps<T, D>& q, const int (&lim)[1], ChunkState<D, 1>& st,
+                                             const Append& ap, bool col_ok, int64_t part_row) {
+  constexpr int TPC = KC / KT;  // tiles per chunk
+  const int j0 = t * KT;
+  tile_store_v<T, D>(v_lds, r);
+  f32x4 s[1][KT / 16];
+  qk_tile_regs<T, D>(r, q, s[0]);
+  if (t + 2 < t_end) {
+    tile_load_regs<T, D, APPEND>(a, hk, j0 + 2 * KT, jlast, ids, r, true, true, ap);
+    tile_block_ids(a, bt, j0 + 3 * KT, jlast, ids);
+  }
+  softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
+  if ((t + 1) % TPC == 0 || t + 1 == t_end) {
+    const float lc = column_sum(st.l[0]);
+    if (col_ok) {
+      const int64_t idx = part_row * a.maxc + t / TPC;
+      if ((lane_id() >> 4) == 0) {
+        a.part_ml[2 * idx] = st.m[0];
+        a.part_ml[2 * idx + 1] = lc;
+      }
+      float* po = a.part_o + idx * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * (lane_id() >> 4)) = st.o[0][dt];
+    }
+    chunk_reset(st);
+  }
+}
+
+template <class T, int D, bool APPEND>
+__global__ __launch_bounds__(64, 2) void decode2_kernel(AttnArgs a) {
+  using G_ = TileGeom<T, D>;
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
+
+  const int b = blockIdx.z;
+  const int hk = blockIdx.y;
+  const int cb = blockIdx.x % a.ncb;
+  const int item = blockIdx.x / a.ncb;
+  const int n = a.seqlens_k[b];
+  const int q0 = a.cu_q[b];
+  const int L = a.cu_q[b + 1] - q0;
+  const int g = a.g;
+  const int ncols = L * g;
+  const int col0 = cb * 16;
+  if (col0 >= ncols) return;
+  const int last_col = min(col0 + 16, ncols) - 1;
+  const int jmax = column_limit(last_col, ncols, g, n, L, a.causal);
+  const int nchunks = jmax > 0 ? (jmax + KC - 1) / KC : 0;
+  const int c_begin = item * a.cpi;
+  const int c_end = min(min(c_begin + a.cpi, nchunks), a.maxc);
+  if (c_begin >= c_end) return;
+  const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
+  const Append ap = make_append<APPEND>(n, L, q0, col0 + 16 >= ncols);
+
+  const int lane = lane_id();
+  const int G = lane >> 4;
+  const int col = col0 + (lane & 15);
+  const int lim[1] = {column_limit(col, ncols, g, n, L, a.causal)};
+  QOps<T, D> q;
+  if (col < ncols) {
+    const int64_t qelem = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * D;
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB;
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + qk_piece_off<T>(k, G));
+  } else {
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k) q.v[k] = u32x4{0, 0, 0, 0};
+  }
+  const int64_t part_row = (int64_t)(q0 + col / g) * a.hq + hk * g + col % g;
+
+  const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
+  const int t_begin = c_begin * (KC / KT);
+  const int t_end = (jlast + KT - 1) / KT;
+  int ids[KT / 16];
+  TileRegs<T, D> ra, rb;
+  tile_block_ids(a, bt, t_begin * KT, jlast, ids);
+  tile_load_regs<T, D, APPEND>(a, hk, t_begin * KT, jlast, ids, ra, true, true, ap);
+  if (t_begin + 1 < t_end) {
+    tile_block_ids(a, bt, (t_begin + 1) * KT, jlast, ids);
+    tile_load_regs<T, D, APPEND>(a, hk, (t_begin + 1) * KT, jlast, ids, rb, true, true, ap);
+  }
+  tile_block_ids(a, bt, (t_begin + 2) * KT, jlast, ids);
+
+  ChunkState<D, 1> st;
+  chunk_reset(st);
+  for (int t = t_begin; t < t_end; t += 2) {
+    decode2_tile<T, D, APPEND>(a, bt, hk, t, t_end, jlast, ids, ra, v_lds, q, lim, st, ap, col < ncols, part_row);
+    if (t + 1 < t_end)
+      decode2_tile<T, D, APPEND>(a, bt, hk, t + 1, t_end, jlast, ids, rb, v_lds, q, lim, st, ap, col < ncols, part_row);
   }
 }
 
@@ -634,7 +759,9 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   }
   dim3 grid(a.ncb * pl.items, pl.hk, pl.batch);
   if (pl.waves == 1) {
-    if constexpr (T::EB == 2) {
+    if constexpr (T::KVB == 1) {
+      hipLaunchKernelGGL((decode2_kernel<T, D, APPEND>), grid, dim3(64), 0, stream, a);
+    } else if constexpr (T::EB == 2) {
       hipLaunchKernelGGL((decode_kernel<T, D, APPEND>), grid, dim3(64), 0, stream, a);
     } else {
       hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true, APPEND>), grid, dim3(64), 0, stream, a);

@@ -84,6 +84,18 @@ template <class T> struct KvRaw { using type = u32x4; };
 template <> struct KvRaw<TFp8> { using type = u32x2; };
 template <class T> constexpr int kKvPiece = 16 * T::KVB / T::EB;
 
+// Byte offset, in a compute-type row, of the 16-byte QK operand piece that
+// lane group G feeds to QK step k (the k-slot map: the 8 elements of the piece
+// fill slots 8G .. 8G+7).  bf16/fp32: piece 64k + 16G (bf16: d = 32k + 8G + e).
+// FP8 caches: 128*(k/2) + 32G + 16*(k%2) (d = 64*(k/2) + 16G + 8*(k%2) + e),
+// so the stored bytes of steps 2j and 2j+1 are one contiguous 16-byte load
+// (twice the bytes per load instruction of the bf16 map).  Every kernel of a
+// type uses its type's map for both Q and K, so the bits never depend on the path.
+template <class T> __device__ __forceinline__ constexpr int qk_piece_off(int k, int G) {
+  if constexpr (T::KVB == 1) return 128 * (k >> 1) + 32 * G + 16 * (k & 1);
+  else return 64 * k + 16 * G;
+}
+
 // Widen stored K/V bytes to the compute type.  FP8 E4M3 -> bf16 is exact
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3 value, subnormals
 // included, is a bf16 value); element e of the piece is byte e.
@@ -166,8 +178,8 @@ __device__ __forceinline__ void chunk_reset(ChunkState<D, NT>& st) {
   }
 }
 
-// Q operands of one column group: lane l holds bytes [64k + 16*(l/16), +16) of
-// its column's query row, k = 0 .. NK-1.  (bf16: the 8 elements that fill MFMA
+// Q operands of one column group: lane l holds bytes [qk_piece_off(k, l/16), +16)
+// of its column's query row, k = 0 .. NK-1 (64k + 16*(l/16) for bf16/fp32).  (bf16: the 8 elements that fill MFMA
 // k-slots 8G..8G+7 of QK step k; fp32: 4 elements feeding 4 MFMA steps.)
 template <class T, int D>
 struct QOps {
@@ -211,12 +223,12 @@ template <class T, int D>
 __device__ __forceinline__ void k_operands_lds(const unsigned char* k_lds, KOps<T, D>& kop) {
   using G_ = TileGeom<T, D>;
   const int lane = lane_id();
-  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH + 16 * (lane >> 4);
+  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH;
 #pragma unroll
   for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k)
-      kop[mt][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + 64 * k);
+      kop[mt][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + qk_piece_off<T>(k, lane >> 4));
 }
 
 // QK^T with the K operands read from the LDS tile one M tile at a time (same
@@ -225,12 +237,13 @@ template <class T, int D>
 __device__ __forceinline__ void qk_tile_lds(const unsigned char* k_lds, const QOps<T, D>& q, f32x4 (&s)[KT / 16]) {
   using G_ = TileGeom<T, D>;
   const int lane = lane_id();
-  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH + 16 * (lane >> 4);
+  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH;
 #pragma unroll
   for (int mt = 0; mt < G_::MT; ++mt) {
     KOps<T, D> kop;
 #pragma unroll
-    for (int k = 0; k < G_::NK; ++k) kop[0][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + 64 * k);
+    for (int k = 0; k < G_::NK; ++k)
+      kop[0][k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + qk_piece_off<T>(k, lane >> 4));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) {
