@@ -23,6 +23,7 @@ gradient identities of softmax (``tests/test_oracle_backward.py``).  No function
 from .paged_kv import (  # noqa: F401
     Layout,
     attention,
+    attention_chunks,
     bf16_bits_to_f64,
     cache_write,
     fp8e4m3_bits_to_f64,

@@ -243,6 +243,52 @@ def attention(q: np.ndarray, k_flat: np.ndarray, v_flat: np.ndarray,
     return out, lse
 
 
+def attention_chunks(q: np.ndarray, k_flat: np.ndarray, v_flat: np.ndarray,
+                     layout: Layout, block_table: np.ndarray, seqlens_k: Sequence[int],
+                     cu_seqlens_q: Sequence[int], causal: bool, softmax_scale: float,
+                     chunk_keys: int, num_chunks: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention restricted to each fixed chunk of global key positions, float64.
+
+    RL-Kernel PR #284, "feat(attention): add CP backward drift validation",
+    section Changes: context parallelism splits the keys into chunks of a fixed
+    size by global position and merges the chunk results in ascending global
+    block index.  For chunk ``c`` (keys ``c*chunk_keys .. (c+1)*chunk_keys - 1``)
+    and each row and query head this is the plain attention over the row's
+    visible keys inside the chunk::
+
+        lse_c = log(sum_{j in J_c} exp(s_j)),   out_c = sum_{j in J_c} exp(s_j - lse_c) v_j
+
+    (``lse_c = -inf``, ``out_c = 0`` when ``J_c`` is empty).  Returns
+    ``(out_c [total_q, nheads, num_chunks, d], lse_c [total_q, nheads, num_chunks])``.
+    The full result follows from them: ``lse = log sum_c exp(lse_c)`` and
+    ``out = sum_c exp(lse_c - lse) out_c``.
+    """
+    Hq, Hk, d = layout.num_heads_q, layout.num_heads_k, layout.head_dim
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    qf = _as_f64(q, layout.dtype).reshape(-1, Hq, d)
+    total_q = qf.shape[0]
+    out = np.zeros((total_q, Hq, num_chunks, d), dtype=np.float64)
+    lse = np.full((total_q, Hq, num_chunks), -np.inf, dtype=np.float64)
+    bt = np.asarray(block_table)
+    for b in range(len(cu) - 1):
+        n = int(seqlens_k[b])
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        L = r1 - r0
+        if L == 0:
+            continue
+        K, V = gather_kv(k_flat, v_flat, layout, bt[b], n)
+        vis = visible_keys(n, L, causal)
+        chunk_of = np.arange(n, dtype=np.int64) // chunk_keys
+        for c in range(num_chunks):
+            vis_c = vis & (chunk_of == c)[None, :]
+            for h in range(Hq):
+                hk = kv_head_of(h, Hq, Hk)
+                w, row_lse = masked_softmax(scores(qf[r0:r1, h, :], K[:, hk, :], softmax_scale), vis_c)
+                out[r0:r1, h, c, :] = w @ V[:, hk, :]
+                lse[r0:r1, h, c] = row_lse
+    return out, lse
+
+
 def scores(q_rows: np.ndarray, k_rows: np.ndarray, softmax_scale: float) -> np.ndarray:
     """``[L, n]`` scaled dot products ``softmax_scale * <q_r, k_j>`` in float64."""
     return softmax_scale * (q_rows @ k_rows.T)

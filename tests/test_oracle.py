@@ -427,3 +427,65 @@ def test_planted_mistakes_are_caught(name, monkeypatch):
         except (AssertionError, IndexError, ValueError):
             failed.append(pin.__name__)
     assert failed, f"planted mistake {name} passed every pin"
+
+
+# ----------------------------------------------------------------------------
+# per-chunk attention (the context-parallel partials)
+# ----------------------------------------------------------------------------
+
+def _chunks(q, pool, bt, seqlens, cu, causal, scale, ck, nc, k_scale=1.0, v_scale=1.0):
+    from tests.oracle_bridge import oracle_pool
+    kf, vf, lay = oracle_pool(pool, q.shape[1], k_scale, v_scale)
+    return oracle.attention_chunks(storage_np(q).reshape(q.shape), kf, vf, lay, np.asarray(bt),
+                                   list(seqlens), [int(x) for x in cu], causal, scale, ck, nc)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_chunk_attention_recombines_to_full(causal):
+    """log-sum-exp over chunks is the full LSE and the LSE-weighted chunk outputs are the full output."""
+    for seed, dt in ((91, "f32"), (92, "bf16")):
+        q, pool, bt, seqlens, cu = tiny_case(seed, dt, "interleaved", 3, 4, 2, 8, 4, 37, [1, 4, 2])
+        out, lse = oracle_attention(q, pool, bt, seqlens, cu, causal, 0.4)
+        for ck in (4, 7, 16):
+            nc = -(-max(seqlens) // ck)
+            oc, lc = _chunks(q, pool, bt, seqlens, cu, causal, 0.4, ck, nc)
+            m = np.max(lc, axis=2, initial=-np.inf)
+            fin = np.isfinite(m)
+            tot = np.where(fin, m + np.log(np.sum(np.exp(lc - np.where(fin, m, 0)[..., None]), axis=2)), -np.inf)
+            assert_close(tot, lse, 1e-12, "recombined lse")
+            wts = np.where(np.isfinite(lc), np.exp(lc - np.where(np.isfinite(tot), tot, 0)[..., None]), 0.0)
+            assert_close(np.sum(wts[..., None] * oc, axis=2), out, 1e-12, "recombined out")
+            # chunks that start past a row's last visible key are empty
+            for b, n in enumerate(seqlens):
+                r0, r1 = int(cu[b]), int(cu[b + 1])
+                for r in range(r1 - r0):
+                    lim = min(n - (r1 - r0) + r + 1, n) if causal else n
+                    for c in range(nc):
+                        if c * ck >= lim:
+                            assert np.all(lc[r0 + r, :, c] == -np.inf) and np.all(oc[r0 + r, :, c] == 0)
+
+
+def test_one_chunk_is_full_attention():
+    q, pool, bt, seqlens, cu = tiny_case(93, "f32", "contiguous", 2, 4, 2, 8, 4, 20, [3, 1])
+    out, lse = oracle_attention(q, pool, bt, seqlens, cu, True, 0.5)
+    oc, lc = _chunks(q, pool, bt, seqlens, cu, True, 0.5, 512, 1)
+    assert np.array_equal(oc[:, :, 0], out) and np.array_equal(lc[:, :, 0], lse)
+
+
+def test_chunk_attention_brute_force():
+    """Each chunk against the decimal brute force run on the chunk's keys alone (a sequence
+    whose keys are that chunk's: the chunk's keys moved to positions 0.. of a fresh cache)."""
+    q, pool, bt, seqlens, cu = tiny_case(94, "f32", "interleaved", 1, 2, 1, 8, 4, 12, [1], [12])
+    ck = 5
+    oc, lc = _chunks(q, pool, bt, seqlens, cu, False, 0.5, ck, 3)
+    kd = pool.k[bt[0].long()].reshape(-1, 1, 8)[:12]
+    vd = pool.v[bt[0].long()].reshape(-1, 1, 8)[:12]
+    for c in range(3):
+        keys = list(range(c * ck, min((c + 1) * ck, 12)))
+        sub = gen.PagedKV(kd[keys].reshape(-1, 1, 1, 8).contiguous(), vd[keys].reshape(-1, 1, 1, 8).contiguous(),
+                          "contiguous", [])
+        sub.storage = [sub.k, sub.v]
+        sbt = torch.arange(len(keys), dtype=torch.int32)[None, :]
+        bo, bl = brute_force(q, sub, sbt, [len(keys)], cu, False, 0.5)
+        assert_close(oc[:, :, c], bo, 1e-12, f"chunk {c} out")
+        assert_close(lc[:, :, c], bl, 1e-12, f"chunk {c} lse")
