@@ -192,6 +192,44 @@ int pkv_attn_forward_append(const void* q, const void* k_new, const void* v_new,
 size_t pkv_attn_workspace_size(const pkv_layout* kv_strides);
 
 /*
+ * Context-parallel share of the forward, and the fold that joins the shares.
+ * RL-Kernel PR #284, "feat(attention): add CP backward drift validation",
+ * section Changes: with context parallelism each rank handles a range of KV
+ * chunks and the partial results are merged in a fixed, ascending global block
+ * (chunk) order, so the result does not depend on the CP world size.
+ *
+ * pkv_attn_chunk_partials computes, for every row and query head, the partial
+ * of each global chunk c in [chunk_begin, chunk_end) that the row can see (the
+ * chunk core of pkv_attn_forward, the same bits), and writes it chunk-major:
+ *   part_ml  device fp32 [max_chunks, total_q * Hq, 2]: (m, l) of the chunk, in the
+ *            library's score units (bf16 and FP8 caches: base 2, m scaled by
+ *            softmax_scale * k_scale * log2(e); fp32: natural units), so
+ *            chunk LSE = (m + log2 l) * ln 2 (fp32 caches: m + ln l); m = -inf if the
+ *            row sees no key of the chunk
+ *   part_o   device fp32 [max_chunks, total_q * Hq, d]: sum over the chunk of
+ *            exp(score - m) * stored V (the chunk output is part_o / l * v_scale)
+ * A rank's range is one contiguous slab of both buffers, ready for an
+ * all-gather.  Slots of chunks a row cannot see are not written.  Arguments
+ * as pkv_attn_forward otherwise; 0 <= chunk_begin <= chunk_end <= max_chunks.
+ *
+ * pkv_attn_merge_partials folds, per row and head, chunks 0 .. ceil(visible
+ * keys / PKV_CHUNK_KEYS) - 1 of such buffers in ascending chunk index and
+ * writes out / lse.  When the buffers hold the partials of every chunk (the
+ * union of the ranks' ranges covers them; precondition), the result is bit
+ * for bit that of pkv_attn_forward on the same inputs, for any split of the
+ * chunk range.  kv_strides supplies shapes, dtype and v_scale.
+ */
+int pkv_attn_chunk_partials(const void* q, const void* k_cache, const void* v_cache,
+                            const pkv_layout* kv_strides, const int32_t* block_table,
+                            const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
+                            float softmax_scale, int32_t chunk_begin, int32_t chunk_end,
+                            int32_t max_chunks, float* part_o, float* part_ml, hipStream_t stream);
+int pkv_attn_merge_partials(const float* part_o, const float* part_ml, int32_t max_chunks,
+                            const pkv_layout* kv_strides, const int32_t* seqlens_k,
+                            const int32_t* cu_seqlens_q, int causal, void* out, float* lse,
+                            hipStream_t stream);
+
+/*
  * Backward of pkv_attn_forward: gradients of out with respect to q and to each
  * sequence's visible keys and values.  RL-Kernel PR #284, "feat(attention):
  * add CP backward drift validation", sections Summary and Changes: a

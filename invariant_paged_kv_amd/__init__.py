@@ -34,6 +34,8 @@ EXPORTS = (
     "pkv_attn_forward_ws",
     "pkv_attn_forward_append",
     "pkv_attn_workspace_size",
+    "pkv_attn_chunk_partials",
+    "pkv_attn_merge_partials",
     "pkv_attn_backward",
     "pkv_attn_backward_workspace_size",
     "pkv_cache_write",
@@ -99,6 +101,10 @@ def lib() -> ctypes.CDLL:
     L.pkv_attn_forward_append.restype = i32
     L.pkv_attn_workspace_size.argtypes = [lay]
     L.pkv_attn_workspace_size.restype = sz
+    L.pkv_attn_chunk_partials.argtypes = [vp, vp, vp, lay, vp, vp, vp, i32, f32, i32, i32, i32, vp, vp, vp]
+    L.pkv_attn_chunk_partials.restype = i32
+    L.pkv_attn_merge_partials.argtypes = [vp, vp, i32, lay, vp, vp, i32, vp, vp, vp]
+    L.pkv_attn_merge_partials.restype = i32
     L.pkv_attn_backward.argtypes = [vp, vp, vp, lay, vp, vp, vp, vp, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.pkv_attn_backward.restype = i32
     L.pkv_attn_backward_workspace_size.argtypes = [lay]
@@ -265,6 +271,58 @@ def attn_forward_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
         _int32(cu_seqlens_q, "cu_seqlens_q").data_ptr(), 1 if causal else 0, float(softmax_scale), out.data_ptr(),
         lse.data_ptr(), ws_ptr, ws_bytes, _stream_handle(q.device))
     _check(rc, "pkv_attn_forward_append")
+    return out, lse
+
+
+def attn_chunk_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                        seqlens_k: torch.Tensor, cu_seqlens_q: torch.Tensor, causal: bool, softmax_scale: float,
+                        chunk_begin: int, chunk_end: int, *, max_seqlen_q: int, max_seqlen_k: int = 0,
+                        max_chunks: Optional[int] = None, part_o: Optional[torch.Tensor] = None,
+                        part_ml: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                        v_scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunk partials of global chunks ``[chunk_begin, chunk_end)`` (one rank's share).
+
+    ``part_o [max_chunks, total_q * Hq, d]`` and ``part_ml [max_chunks, total_q * Hq, 2]``
+    fp32, chunk-major; allocated (uninitialised) when not given.
+    """
+    if q.dtype != query_dtype(k_cache.dtype):
+        raise TypeError("q dtype does not match the cache (bf16 queries for an FP8 cache)")
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k,
+                      k_scale=k_scale, v_scale=v_scale)
+    if max_chunks is None:
+        mk = max_seqlen_k or block_table.shape[1] * k_cache.shape[1]
+        max_chunks = max(1, -(-mk // CHUNK_KEYS))
+    rows = q.shape[0] * q.shape[1]
+    if part_o is None:
+        part_o = torch.empty((max_chunks, rows, q.shape[2]), dtype=torch.float32, device=q.device)
+    if part_ml is None:
+        part_ml = torch.empty((max_chunks, rows, 2), dtype=torch.float32, device=q.device)
+    rc = lib().pkv_attn_chunk_partials(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(lay),
+        _int32(block_table, "block_table").data_ptr(), _int32(seqlens_k, "seqlens_k").data_ptr(),
+        _int32(cu_seqlens_q, "cu_seqlens_q").data_ptr(), 1 if causal else 0, float(softmax_scale), int(chunk_begin),
+        int(chunk_end), int(max_chunks), part_o.data_ptr(), part_ml.data_ptr(), _stream_handle(q.device))
+    _check(rc, "pkv_attn_chunk_partials")
+    return part_o, part_ml
+
+
+def attn_merge_partials(part_o: torch.Tensor, part_ml: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, block_table: torch.Tensor, seqlens_k: torch.Tensor,
+                        cu_seqlens_q: torch.Tensor, causal: bool, *, max_seqlen_q: int, max_seqlen_k: int = 0,
+                        v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fold chunk partials in ascending chunk order into ``(out, lse)`` (shapes from ``q``)."""
+    lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k,
+                      v_scale=v_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    rc = lib().pkv_attn_merge_partials(part_o.data_ptr(), part_ml.data_ptr(), int(part_o.shape[0]), ctypes.byref(lay),
+                                       _int32(seqlens_k, "seqlens_k").data_ptr(),
+                                       _int32(cu_seqlens_q, "cu_seqlens_q").data_ptr(), 1 if causal else 0,
+                                       out.data_ptr(), lse.data_ptr(), _stream_handle(q.device))
+    _check(rc, "pkv_attn_merge_partials")
     return out, lse
 
 

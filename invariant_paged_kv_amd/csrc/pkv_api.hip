@@ -213,6 +213,10 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.ncb = p.ncb;
   a.maxc = p.maxc;
   a.cpi = p.cpi;
+  a.chunk0 = 0;
+  a.chunk1 = p.maxc;
+  a.ps_row = p.maxc;
+  a.ps_chunk = 1;
   a.causal = causal ? 1 : 0;
   a.mul = score_mul(*l, softmax_scale);
   a.v_scale = kv_scale(l->v_scale);
@@ -227,6 +231,99 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
     if (e == hipSuccess && fe != hipSuccess) e = fe;
   }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// Context-parallel share: the chunk partials of global chunks [c0, c1), chunk-major.
+int run_partials(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* l,
+                 const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
+                 float softmax_scale, int32_t c0, int32_t c1, int32_t max_chunks, float* part_o, float* part_ml,
+                 hipStream_t stream) {
+  int rc = validate(l);
+  if (rc) return rc;
+  rc = check_attn_ptrs(q, k_cache, v_cache, block_table, seqlens_k, cu_seqlens_q, part_o, part_ml, *l);
+  if (rc) return rc;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(PKV_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (max_chunks < 1 || c0 < 0 || c0 > c1 || c1 > max_chunks)
+    return fail(PKV_ERR_SHAPE, "need 0 <= chunk_begin <= chunk_end <= max_chunks, max_chunks >= 1");
+  if (!aligned16(part_ml)) return fail(PKV_ERR_ALIGN, "part_ml must be 16-byte aligned");
+  if (l->batch == 0 || l->total_q == 0 || c0 == c1) return ok();
+  const int g = l->num_heads_q / l->num_heads_k;
+  const int64_t cols = static_cast<int64_t>(l->max_seqlen_q) * g;
+  const int waves = cols <= 16 ? 1 : 4;
+  int64_t cpi = g_opt_split_chunks.load();
+  if (cpi <= 0) cpi = 1;
+  pkv::LaunchPlan lp{};
+  lp.full = false;
+  lp.skip_merge = true;
+  lp.waves = waves;
+  lp.items = static_cast<int>((c1 - c0 + cpi - 1) / cpi);
+  lp.batch = l->batch;
+  lp.hk = l->num_heads_k;
+  lp.total_q = l->total_q;
+  pkv::AttnArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.block_table = block_table;
+  a.seqlens_k = seqlens_k;
+  a.cu_q = cu_seqlens_q;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.kbs = l->k_block_stride;
+  a.kss = l->k_slot_stride;
+  a.khs = l->k_head_stride;
+  a.vbs = l->v_block_stride;
+  a.vss = l->v_slot_stride;
+  a.vhs = l->v_head_stride;
+  a.hq = l->num_heads_q;
+  a.g = g;
+  a.bs = l->block_size;
+  a.mbps = l->max_blocks_per_seq;
+  a.ncb = static_cast<int>(std::max<int64_t>(1, (cols + 16 * waves - 1) / (16 * waves)));
+  a.maxc = max_chunks;
+  a.cpi = static_cast<int>(cpi);
+  a.chunk0 = c0;
+  a.chunk1 = c1;
+  a.ps_row = 1;
+  a.ps_chunk = l->total_q * l->num_heads_q;
+  a.causal = causal ? 1 : 0;
+  a.mul = score_mul(*l, softmax_scale);
+  a.v_scale = kv_scale(l->v_scale);
+  pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
+  hipError_t e = pkv::launch_attention(a, lp, l->dtype, l->head_dim, stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "partials launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int run_merge(const float* part_o, const float* part_ml, int32_t max_chunks, const pkv_layout* l,
+              const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal, void* out, float* lse,
+              hipStream_t stream) {
+  int rc = validate(l);
+  if (rc) return rc;
+  if (max_chunks < 1) return fail(PKV_ERR_SHAPE, "max_chunks must be >= 1");
+  if (l->total_q > 0 && (!part_o || !part_ml || !out || !lse)) return fail(PKV_ERR_NULL, "a merge pointer is NULL");
+  if (l->batch > 0 && (!seqlens_k || !cu_seqlens_q)) return fail(PKV_ERR_NULL, "seqlens_k or cu_seqlens_q is NULL");
+  if (!aligned16(part_o) || !aligned16(part_ml)) return fail(PKV_ERR_ALIGN, "part_o and part_ml must be 16-byte aligned");
+  if (l->batch == 0 || l->total_q == 0) return ok();
+  pkv::MergeArgs m{};
+  m.cu_q = cu_seqlens_q;
+  m.seqlens_k = seqlens_k;
+  m.part_o = part_o;
+  m.part_ml = part_ml;
+  m.out = out;
+  m.lse = lse;
+  m.total_q = l->total_q;
+  m.batch = l->batch;
+  m.hq = l->num_heads_q;
+  m.maxc = max_chunks;
+  m.causal = causal ? 1 : 0;
+  m.v_scale = kv_scale(l->v_scale);
+  m.ps_row = 1;
+  m.ps_chunk = l->total_q * l->num_heads_q;
+  hipError_t e = pkv::launch_merge(m, l->dtype, l->head_dim, stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -361,6 +458,20 @@ int pkv_attn_backward(const void* q, const void* k_cache, const void* v_cache, c
 size_t pkv_attn_backward_workspace_size(const pkv_layout* kv_strides) {
   if (validate(kv_strides) != PKV_OK) return 0;
   return backward_ws_bytes(*kv_strides);
+}
+
+int pkv_attn_chunk_partials(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* kv_strides,
+                            const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q,
+                            int causal, float softmax_scale, int32_t chunk_begin, int32_t chunk_end,
+                            int32_t max_chunks, float* part_o, float* part_ml, hipStream_t stream) {
+  return run_partials(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, causal, softmax_scale,
+                      chunk_begin, chunk_end, max_chunks, part_o, part_ml, stream);
+}
+
+int pkv_attn_merge_partials(const float* part_o, const float* part_ml, int32_t max_chunks,
+                            const pkv_layout* kv_strides, const int32_t* seqlens_k, const int32_t* cu_seqlens_q,
+                            int causal, void* out, float* lse, hipStream_t stream) {
+  return run_merge(part_o, part_ml, max_chunks, kv_strides, seqlens_k, cu_seqlens_q, causal, out, lse, stream);
 }
 
 int pkv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const pkv_layout* l,

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   const int nchunks = jmax > 0 ? (jmax + KC - 1) / KC : 0;
   int c_begin = 0, c_end = nchunks;
   if constexpr (SPLIT) {
-    c_begin = item * a.cpi;
-    c_end = min(min(c_begin + a.cpi, nchunks), a.maxc);
+    c_begin = a.chunk0 + item * a.cpi;
+    c_end = min(min(c_begin + a.cpi, nchunks), a.chunk1);
     if (c_begin >= c_end) return;
   }
 
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
       if constexpr (SPLIT) {
         const int col = cols[nt];
         if (col < ncols) {
-          const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.maxc + c;
+          const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.ps_row + c * a.ps_chunk;
           if (G == 0) {
             a.part_ml[2 * idx] = st.m[nt];
             a.part_ml[2 * idx + 1] = lc;
@@ -506,8 +506,8 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   const int last_col = min(col0 + 16, ncols) - 1;
   const int jmax = column_limit(last_col, ncols, g, n, L, a.causal);
   const int nchunks = jmax > 0 ? (jmax + KC - 1) / KC : 0;
-  const int c_begin = item * a.cpi;
-  const int c_end = min(min(c_begin + a.cpi, nchunks), a.maxc);
+  const int c_begin = a.chunk0 + item * a.cpi;
+  const int c_end = min(min(c_begin + a.cpi, nchunks), a.chunk1);
   if (c_begin >= c_end) return;
   const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
   const Append ap = make_append<APPEND>(n, L, q0, col0 + 16 >= ncols);
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
     }
     const float lc = column_sum(st.l[0]);
     if (col < ncols) {
-      const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.maxc + c;
+      const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.ps_row + c * a.ps_chunk;
       if (G == 0) {
         a.part_ml[2 * idx] = st.m[0];
         a.part_ml[2 * idx + 1] = lc;
@@ -593,7 +593,7 @@ __device__ __forceinline__ void decode2_tile(const AttnArgs& a, const int32_t* b
   if ((t + 1) % TPC == 0 || t + 1 == t_end) {
     const float lc = column_sum(st.l[0]);
     if (col_ok) {
-      const int64_t idx = part_row * a.maxc + t / TPC;
+      const int64_t idx = part_row * a.ps_row + static_cast<int64_t>(t / TPC) * a.ps_chunk;
       if ((lane_id() >> 4) == 0) {
         a.part_ml[2 * idx] = st.m[0];
         a.part_ml[2 * idx + 1] = lc;
@@ -625,8 +625,8 @@ __global__ __launch_bounds__(64, 2) void decode2_kernel(AttnArgs a) {
   const int last_col = min(col0 + 16, ncols) - 1;
   const int jmax = column_limit(last_col, ncols, g, n, L, a.causal);
   const int nchunks = jmax > 0 ? (jmax + KC - 1) / KC : 0;
-  const int c_begin = item * a.cpi;
-  const int c_end = min(min(c_begin + a.cpi, nchunks), a.maxc);
+  const int c_begin = a.chunk0 + item * a.cpi;
+  const int c_end = min(min(c_begin + a.cpi, nchunks), a.chunk1);
   if (c_begin >= c_end) return;
   const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
   const Append ap = make_append<APPEND>(n, L, q0, col0 + 16 >= ncols);
@@ -704,15 +704,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   float O[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) O[e] = 0.f;
-  const int64_t base = w * a.maxc;
+  const int64_t base = w * a.ps_row;
   for (int c0 = 0; c0 < nck; c0 += PF) {
     float mc[PF], lc[PF], oc[PF][EPL];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int c = min(c0 + i, nck - 1);
-      mc[i] = a.part_ml[2 * (base + c)];
-      lc[i] = a.part_ml[2 * (base + c) + 1];
-      const float* po = a.part_o + (base + c) * D + e0;
+      const int64_t pi = base + c * a.ps_chunk;
+      mc[i] = a.part_ml[2 * pi];
+      lc[i] = a.part_ml[2 * pi + 1];
+      const float* po = a.part_o + pi * D + e0;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) oc[i][e] = active ? po[e] : 0.f;
     }
@@ -770,7 +771,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
     hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, true, APPEND>), grid, dim3(256), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || pl.skip_merge) return e;
   MergeArgs m;
   m.cu_q = a.cu_q;
   m.seqlens_k = a.seqlens_k;
@@ -782,6 +783,8 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   m.batch = pl.batch;
   m.hq = a.hq;
   m.maxc = a.maxc;
+  m.ps_row = a.ps_row;
+  m.ps_chunk = a.ps_chunk;
   m.causal = a.causal;
   m.v_scale = a.v_scale;
   const int64_t waves = pl.total_q * a.hq;
@@ -800,6 +803,22 @@ static hipError_t launch_attention_t(const AttnArgs& a, const LaunchPlan& pl, in
     return d == 128 ? launch_attn_t<TFp8, 128, APPEND>(a, pl, stream) : launch_attn_t<TFp8, 64, APPEND>(a, pl, stream);
   }
   return d == 128 ? launch_attn_t<TF32, 128, APPEND>(a, pl, stream) : launch_attn_t<TF32, 64, APPEND>(a, pl, stream);
+}
+
+template <class T, int D>
+static hipError_t launch_merge_t(const MergeArgs& m, hipStream_t stream) {
+  const int64_t waves = m.total_q * m.hq;
+  if (waves == 0) return hipSuccess;
+  dim3 mgrid(static_cast<unsigned>((waves * kMergeWavesPerRow + 3) / 4));
+  hipLaunchKernelGGL((merge_kernel<T, D>), mgrid, dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& m, int dtype, int d, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (dtype == 0) return d == 128 ? launch_merge_t<TF32, 128>(m, stream) : launch_merge_t<TF32, 64>(m, stream);
+  // bf16 and FP8 caches share the bf16 output path
+  return d == 128 ? launch_merge_t<TBf16, 128>(m, stream) : launch_merge_t<TBf16, 64>(m, stream);
 }
 
 hipError_t launch_attention(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream) {

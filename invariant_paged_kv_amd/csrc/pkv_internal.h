@@ -24,6 +24,10 @@ struct AttnArgs {
   int32_t ncb;     // column blocks per (sequence, KV head)
   int32_t maxc;    // chunk capacity of the partial buffers
   int32_t cpi;     // chunks per split work item
+  int32_t chunk0;  // split path: global chunks [chunk0, chunk1) are computed
+  int32_t chunk1;
+  int64_t ps_row;    // partial index of (row*Hq + head, chunk c) = rowhead*ps_row + c*ps_chunk
+  int64_t ps_chunk;
   int32_t causal;
   float mul;       // score multiplier: scale * k_scale (fp32), times log2(e) for base-2 types
   float v_scale;   // stored-V scale, applied at the final write (1: unscaled)
@@ -49,12 +53,14 @@ struct MergeArgs {
   int64_t total_q;
   int32_t batch, hq, maxc, causal;
   float v_scale;
+  int64_t ps_row, ps_chunk;  // partial layout, as in AttnArgs
 };
 
 struct LaunchPlan {
   bool full;       // prefill kernel (true) or split kernels + merge (false)
   bool full4;      // full path, bf16: 4-wave single-buffered kernel instead of the 8-wave pipelined one
   bool append;     // fused append of k_new / v_new
+  bool skip_merge; // split path: write the chunk partials only
   int waves;       // split path: waves per work group (1 or 4)
   int items;       // split path: work items per column block along the keys
   int batch, hk;
@@ -115,6 +121,7 @@ struct BwdPlan {
 
 hipError_t launch_attention(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, const BwdPlan& pl, int dtype, int d, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& m, int dtype, int d, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, int elem_bytes, int64_t total_new, hipStream_t stream);
 
 }  // namespace pkv

@@ -155,3 +155,22 @@ def test_backward_workspace_size():
     lay = good_layout(total_q=100)
     assert L.pkv_attn_backward_workspace_size(ctypes.byref(lay)) == -(-100 * 16 * 4 // 256) * 256
     assert L.pkv_attn_backward_workspace_size(ctypes.byref(good_layout(head_dim=3))) == 0
+
+
+def test_chunk_partials_and_merge_reject_bad_arguments():
+    L = pkv.lib()
+    lay = good_layout(total_q=2)
+
+    def part(c0, c1, mc, po=96, pm=112):
+        return L.pkv_attn_chunk_partials(16, 16, 32, ctypes.byref(lay), 64, 64, 64, 1, 0.1, c0, c1, mc, po, pm, None)
+
+    assert part(0, 3, 2) == -2          # chunk_end past max_chunks
+    assert part(2, 1, 4) == -2          # empty range reversed
+    assert part(-1, 1, 4) == -2
+    assert part(0, 1, 0) == -2
+    assert part(0, 1, 4, po=None) == -1
+    assert part(0, 1, 4, pm=104) == -4  # part_ml must be 16-byte aligned
+    assert part(1, 1, 4) == 0           # an idle rank: nothing to do
+    assert L.pkv_attn_merge_partials(96, 112, 0, ctypes.byref(lay), 64, 64, 1, 48, 64, None) == -2
+    assert L.pkv_attn_merge_partials(None, 112, 4, ctypes.byref(lay), 64, 64, 1, 48, 64, None) == -1
+    assert L.pkv_attn_merge_partials(96, 104, 4, ctypes.byref(lay), 64, 64, 1, 48, 64, None) == -4
