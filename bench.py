@@ -174,7 +174,8 @@ def main():
     if not args.no_prefill:
         result["prefill"], result["backward"] = bench_prefill(torch, pkv, gen)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale)
+        result["cpu_baseline"], result["oracle_parity"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale,
+                                                                       out, lse)
     print(json.dumps(result), flush=True)
 
 
@@ -316,8 +317,12 @@ def bench_prefill(torch, pkv, gen, reps: int = 3):
     return fwd, bwd_res
 
 
-def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, budget_s: float = 12.0):
-    """The float64 oracle on whole sequences of the same decode step, timed on the host."""
+def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, out, lse, budget_s: float = 12.0):
+    """The float64 oracle on whole sequences of the same decode step, timed on the host.
+
+    The oracle's results for those sequences are also compared with the GPU's
+    out / lse of the same step (max-abs errors reported next to the timing).
+    """
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -325,6 +330,9 @@ def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, budget_s: float =
 
     nblk = math.ceil(N / BS)
     done, spent, seqs = 0, 0.0, 0
+    err_o = err_l = 0.0
+    gout = out.double().cpu().numpy()
+    glse = lse.double().cpu().numpy()
     B, HQ = q.shape[0], q.shape[1]
     for b in range(B):
         ids = bt[b, :nblk].long()
@@ -336,8 +344,10 @@ def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, budget_s: float =
         lay = oracle.Layout("bf16", HQ, HK, D, BS, 0, (BS * row, row, D), 0, (BS * row, row, D))
         qh = q[b:b + 1].cpu().view(torch.int16).numpy().view(np.uint16)
         t0 = time.perf_counter()
-        oracle.attention(qh, kf, vf, lay, np.arange(nblk, dtype=np.int32)[None, :], [N], [0, 1], True, scale)
+        oo, ol = oracle.attention(qh, kf, vf, lay, np.arange(nblk, dtype=np.int32)[None, :], [N], [0, 1], True, scale)
         spent += time.perf_counter() - t0
+        err_o = max(err_o, float(np.max(np.abs(gout[b] - oo[0]))))
+        err_l = max(err_l, float(np.max(np.abs(glse[b] - ol[0]))))
         seqs += 1
         done += N * HK * D * 2 * 2
         if spent >= budget_s:
@@ -345,7 +355,8 @@ def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, budget_s: float =
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(done / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{seqs} of {B} sequences of one decode step (all {HQ} heads, {N} keys each), "
-                      f"{spent:.1f} s"}
+                      f"{spent:.1f} s"}, {"out_max_abs": err_o, "lse_max_abs": err_l, "sequences": seqs,
+                                           "tolerance": {"out": 2e-2, "lse": 1e-3}}
 
 
 if __name__ == "__main__":
