@@ -40,6 +40,10 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
   }
 }
 
+#ifndef PKV_ATTN_XCD
+#define PKV_ATTN_XCD 1
+#endif
+
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND>
 __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
@@ -48,14 +52,27 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   unsigned char* k_lds = lds;
   unsigned char* v_lds = lds + G_::KBYTES;
 
-  const int b = blockIdx.z;
-  const int hk = blockIdx.y;
+  int b = blockIdx.z;
+  int hk = blockIdx.y;
   int cb, item;
   if constexpr (SPLIT) {
     cb = blockIdx.x % a.ncb;
     item = blockIdx.x / a.ncb;
   } else {
+#if PKV_ATTN_XCD
+    // Work groups are dispatched round-robin over the 8 XCDs; renumber them so
+    // one XCD runs consecutive column blocks of the same (sequence, KV head)
+    // and its L2 serves the K/V tiles they share (as in prefill_kernel).
+    const int nwg = gridDim.x * gridDim.y * gridDim.z;
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int full8 = nwg / 8 * 8;
+    const int w = lin < full8 ? (lin % 8) * (nwg / 8) + lin / 8 : lin;
+    b = w / (gridDim.x * gridDim.y);
+    hk = (w / gridDim.x) % gridDim.y;
+    cb = a.ncb - 1 - w % gridDim.x;  // heaviest causal blocks first
+#else
     cb = a.ncb - 1 - static_cast<int>(blockIdx.x);  // heaviest causal blocks first
+#endif
     item = 0;
   }
   const int n = a.seqlens_k[b];

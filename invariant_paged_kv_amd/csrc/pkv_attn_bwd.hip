@@ -43,6 +43,30 @@ __device__ __forceinline__ float elem_f32(const void* p, int64_t i, int eb) {
   return static_cast<const float*>(p)[i];
 }
 
+#ifndef PKV_BWD_XCD
+#define PKV_BWD_XCD 1
+#endif
+
+// Work groups are dispatched round-robin over the 8 XCDs (each with its own
+// L2); renumber them so that one XCD runs consecutive blocks of the same
+// (sequence, KV head), whose shared tiles its L2 then serves.  Returns the
+// (x, y, z) the work group takes on.
+__device__ __forceinline__ void xcd_order(int& x, int& y, int& z) {
+#if PKV_BWD_XCD
+  const int nwg = gridDim.x * gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int full8 = nwg / 8 * 8;
+  const int w = lin < full8 ? (lin % 8) * (nwg / 8) + lin / 8 : lin;
+  x = w % gridDim.x;
+  y = (w / gridDim.x) % gridDim.y;
+  z = w / (gridDim.x * gridDim.y);
+#else
+  x = blockIdx.x;
+  y = blockIdx.y;
+  z = blockIdx.z;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // delta[w] = <dout[w], out[w]> for each (row, head) w, in fp32: 16 lanes per w,
 // each lane sums D/16 consecutive elements in ascending order, then a fixed
@@ -150,9 +174,9 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
   unsigned char* k_lds = lds;
   unsigned char* v_lds = lds + G_::KBYTES;
 
-  const int b = blockIdx.z;
-  const int hk = blockIdx.y;
-  const int cb = a.ncb - 1 - static_cast<int>(blockIdx.x);  // heaviest causal blocks first
+  int bx, hk, b;
+  xcd_order(bx, hk, b);
+  const int cb = a.ncb - 1 - bx;  // heaviest causal blocks first
   const int n = a.seqlens_k[b];
   const int q0 = a.cu_q[b];
   const int L = a.cu_q[b + 1] - q0;
@@ -324,9 +348,9 @@ __global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(Bw
   constexpr int BUF = 2 * C_::BYTES + 2 * kBwdCols * sizeof(float);
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
 
-  const int b = blockIdx.z;
-  const int hk = blockIdx.y;
-  const int key0 = static_cast<int>(blockIdx.x) * 16 * W;
+  int bx, hk, b;
+  xcd_order(bx, hk, b);
+  const int key0 = bx * 16 * W;
   const int n = a.seqlens_k[b];
   if (key0 >= n) return;
   const int q0 = a.cu_q[b];
