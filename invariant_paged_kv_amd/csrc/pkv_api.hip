@@ -120,17 +120,15 @@ Plan make_plan(const pkv_layout& l) {
     full = full_items >= 512;
   }
   if (!full) waves = cols <= 16 ? 1 : 4;
-  // bf16 full path: with many column blocks, the single-buffered 4-wave kernel
-  // (three work groups per CU) beats the pipelined 8-wave one (one per CU);
-  // with few long blocks (long keys, few rows) the pipelined one wins.
+  // bf16/FP8 full path: 4 waves x 32 columns per work group (two column
+  // groups per wave: every K/V tile read from LDS serves 32 columns) unless
+  // the pipelined 8-wave x 16-column kernel is asked for; both give the same
+  // bits.  Measured on the 8 x 8192 prefill 609-618 against 441 TFLOP/s, and
+  // on 64 rows x 131072 keys 560-565 against 366.
   bool full4 = false;
-  if (full && l.dtype == PKV_BF16) {
-    const int64_t opt = g_opt_full_kernel.load();
-    const int64_t blocks64 = static_cast<int64_t>(l.batch) * l.num_heads_k * ((cols + 63) / 64);
-    full4 = opt == 2 || (opt == 0 && blocks64 >= 2048);
-  }
+  if (full && l.dtype != PKV_F32) full4 = g_opt_full_kernel.load() != 1;
   p.lp.full4 = full4;
-  const int cols_per_block = full ? (full4 ? 64 : 128) : 16 * waves;
+  const int cols_per_block = full ? 128 : 16 * waves;
   p.ncb = static_cast<int>(std::max<int64_t>(1, (cols + cols_per_block - 1) / cols_per_block));
   int64_t cpi = g_opt_split_chunks.load();
   if (cpi <= 0) cpi = 1;

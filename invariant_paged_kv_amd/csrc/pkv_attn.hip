@@ -766,7 +766,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
     dim3 grid(a.ncb, pl.hk, pl.batch);
     if constexpr (T::EB == 2) {
       if (pl.full4) {
-        hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, false, APPEND>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false, APPEND>), grid, dim3(256), 0, stream, a);
       } else {
         hipLaunchKernelGGL((prefill_kernel<T, D, 8, APPEND>), grid, dim3(512), 0, stream, a);
       }

@@ -58,7 +58,7 @@ struct MergeArgs {
 
 struct LaunchPlan {
   bool full;       // prefill kernel (true) or split kernels + merge (false)
-  bool full4;      // full path, bf16: 4-wave single-buffered kernel instead of the 8-wave pipelined one
+  bool full4;      // full path, bf16/FP8: 4 waves x 32 columns (attn_kernel) instead of the 8-wave pipelined kernel
   bool append;     // fused append of k_new / v_new
   bool skip_merge; // split path: write the chunk partials only
   int waves;       // split path: waves per work group (1 or 4)
