@@ -398,7 +398,7 @@ int run_backward(const void* q, const void* k_cache, const void* v_cache, const 
   b.delta = static_cast<float*>(ws);
   b.scale = softmax_scale;
   b.nkb = total_k > 0 ? static_cast<int>((mk + 16 * kWaves - 1) / (16 * kWaves)) : 0;
-  pkv::BwdPlan pl{l->batch, l->num_heads_k, l->total_q};
+  pkv::BwdPlan pl{l->batch, l->num_heads_k, l->total_q, cols, mk};
   hipError_t e = pkv::launch_backward(b, pl, l->dtype, l->head_dim, stream);
   if (allocated) {
     hipError_t fe = hipFreeAsync(ws, stream);

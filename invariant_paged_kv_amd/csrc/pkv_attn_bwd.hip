@@ -46,6 +46,12 @@ __device__ __forceinline__ float elem_f32(const void* p, int64_t i, int eb) {
 #ifndef PKV_BWD_XCD
 #define PKV_BWD_XCD 1
 #endif
+#ifndef PKV_DQ_NT
+#define PKV_DQ_NT 2
+#endif
+#ifndef PKV_DKDV_KW
+#define PKV_DKDV_KW 1
+#endif
 
 // Work groups are dispatched round-robin over the 8 XCDs (each with its own
 // L2); renumber them so that one XCD runs consecutive blocks of the same
@@ -166,10 +172,11 @@ __device__ __forceinline__ void row_operands_global(const void* base, int64_t ro
 //   P = exp(S * mul - lse), dS = P (dP - delta) (0 for invisible keys),
 //   dQ^T += K^T dS^T (head dim as M, keys as the k-dimension, as the forward's PV).
 // ---------------------------------------------------------------------------
-template <class T, int D, int W>
+template <class T, int D, int W, int NT>
 __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
   const AttnArgs& a = ba.f;
   using G_ = TileGeom<T, D>;
+  constexpr int COLS = 16 * W * NT;
   __shared__ __attribute__((aligned(16))) unsigned char lds[G_::BYTES];
   unsigned char* k_lds = lds;
   unsigned char* v_lds = lds + G_::KBYTES;
@@ -182,27 +189,37 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
   const int L = a.cu_q[b + 1] - q0;
   const int g = a.g;
   const int ncols = L * g;
-  const int col0 = cb * 16 * W;
+  const int col0 = cb * COLS;
   if (col0 >= ncols) return;
-  const int last_col = min(col0 + 16 * W, ncols) - 1;
+  const int last_col = min(col0 + COLS, ncols) - 1;
   const int jmax = column_limit(last_col, ncols, g, n, L, a.causal);
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int G = lane >> 4;
-  const int col = col0 + 16 * wave + (lane & 15);
-  const bool exists = col < ncols;
-  const int lim = exists ? column_limit(col, ncols, g, n, L, a.causal) : 0;
-  const int64_t rh = static_cast<int64_t>(q0 + col / g) * a.hq + hk * g + col % g;
-  QOps<T, D> q, dout;
-  row_operands_global<T, D>(a.q, rh, exists, q);
-  row_operands_global<T, D>(ba.dout, rh, exists, dout);
-  const float lse_u = (exists && lim > 0) ? lse_units<T>(ba.lse[rh]) : 0.f;
-  const float dlt = exists ? ba.delta[rh] : 0.f;
-
-  f32x4 acc[D / 16];
+  // NT groups of 16 columns per wave: every K/V operand read from LDS serves them all.
+  int lim[NT];
+  bool exists[NT];
+  int64_t rh[NT];
+  float lse_u[NT], dlt[NT];
+  QOps<T, D> q[NT], dout[NT];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = col0 + (wave * NT + nt) * 16 + (lane & 15);
+    exists[nt] = col < ncols;
+    lim[nt] = exists[nt] ? column_limit(col, ncols, g, n, L, a.causal) : 0;
+    rh[nt] = static_cast<int64_t>(q0 + col / g) * a.hq + hk * g + col % g;
+    row_operands_global<T, D>(a.q, rh[nt], exists[nt], q[nt]);
+    row_operands_global<T, D>(ba.dout, rh[nt], exists[nt], dout[nt]);
+    lse_u[nt] = (exists[nt] && lim[nt] > 0) ? lse_units<T>(ba.lse[rh[nt]]) : 0.f;
+    dlt[nt] = exists[nt] ? ba.delta[rh[nt]] : 0.f;
+  }
+
+  f32x4 acc[NT][D / 16];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.mbps;
   const Append none;
@@ -210,29 +227,42 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
     __syncthreads();
     load_tile<T, D, W, false>(a, bt, hk, j0, jmax, k_lds, v_lds, none);
     __syncthreads();
-    f32x4 s[G_::MT], dp[G_::MT];
-    {
-      KOps<T, D> op;
-      row_operands_lds<T, D>(k_lds, G_::KPITCH, op);
-      qk_tile<T, D>(op, q, s);
-      row_operands_lds<T, D>(v_lds, G_::VPITCH, op);
-      qk_tile<T, D>(op, dout, dp);
+    f32x4 s[NT][G_::MT], dp[NT][G_::MT];
+#pragma unroll
+    for (int mt = 0; mt < G_::MT; ++mt) {
+      u32x4 kx[G_::NK], vx[G_::NK];
+      const unsigned char* kr = k_lds + (16 * mt + (lane & 15)) * G_::KPITCH + 16 * G;
+      const unsigned char* vr = v_lds + (16 * mt + (lane & 15)) * G_::VPITCH + 16 * G;
+#pragma unroll
+      for (int k = 0; k < G_::NK; ++k) {
+        kx[k] = *reinterpret_cast<const u32x4*>(kr + 64 * k);
+        vx[k] = *reinterpret_cast<const u32x4*>(vr + 64 * k);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        s[nt][mt] = dot_tile<T, G_::NK>(kx, q[nt].v);
+        dp[nt][mt] = dot_tile<T, G_::NK>(vx, dout[nt].v);
+      }
     }
-    if (__all(j0 + KT <= lim)) {  // the whole tile is visible to every lane: no mask
 #pragma unroll
-      for (int mt = 0; mt < G_::MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt) {
+      if (__all(j0 + KT <= lim[nt])) {  // the whole tile is visible to every lane: no mask
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[mt][i] = pkv_exp<T>(fmaf(s[mt][i], a.mul, -lse_u)) * (dp[mt][i] - dlt);
-    } else {
+        for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < G_::MT; ++mt)
+          for (int i = 0; i < 4; ++i)
+            s[nt][mt][i] = pkv_exp<T>(fmaf(s[nt][mt][i], a.mul, -lse_u[nt])) * (dp[nt][mt][i] - dlt[nt]);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = j0 + 16 * mt + 4 * G + i;
-          const bool vis = key < lim;
-          const float p = vis ? pkv_exp<T>(fmaf(s[mt][i], a.mul, -lse_u)) : 0.f;
-          s[mt][i] = vis ? p * (dp[mt][i] - dlt) : 0.f;  // dS^T
-        }
+        for (int mt = 0; mt < G_::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j0 + 16 * mt + 4 * G + i;
+            const bool vis = key < lim[nt];
+            const float p = vis ? pkv_exp<T>(fmaf(s[nt][mt][i], a.mul, -lse_u[nt])) : 0.f;
+            s[nt][mt][i] = vis ? p * (dp[nt][mt][i] - dlt[nt]) : 0.f;  // dS^T
+          }
+      }
     }
     if constexpr (T::EB == 2) {
 #pragma unroll
@@ -240,7 +270,9 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
 #pragma unroll
         for (int ks = 0; ks < KT / 32; ++ks) {
           const u32x4 kt = v_operand_bf16(k_lds, G_::KPITCH, ks, dt);
-          acc[dt] = mfma_bf16(kt, pack_bf16(s[2 * ks], s[2 * ks + 1]), acc[dt]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[nt][dt] = mfma_bf16(kt, pack_bf16(s[nt][2 * ks], s[nt][2 * ks + 1]), acc[nt][dt]);
         }
     } else {
       const unsigned char* colp = k_lds + 4 * (lane & 15);
@@ -251,11 +283,14 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float kt = *reinterpret_cast<const float*>(colp + (16 * mt + 4 * G + i) * G_::KPITCH + 4 * 16 * dt);
-            acc[dt] = mfma_f32(kt, s[mt][i], acc[dt]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma_f32(kt, s[nt][mt][i], acc[nt][dt]);
           }
     }
   }
-  if (exists) store_grad<T, D>(ba.dq, rh * D, acc, ba.scale);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    if (exists[nt]) store_grad<T, D>(ba.dq, rh[nt] * D, acc[nt], ba.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -338,9 +373,10 @@ __device__ __forceinline__ void col_stage_store(unsigned char* buf, const ColSta
 
 // Each 32-column step is computed from one LDS buffer while the next step's
 // rows are in flight in registers; they go to the other buffer afterwards, and
-// one barrier per step separates the two.
-template <class T, int D, int W>
-__global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(BwdArgs ba) {
+// one barrier per step separates the two.  Each wave owns KW tiles of 16 keys:
+// every Q / dO operand read from LDS serves all of them.
+template <class T, int D, int W, int KW>
+__global__ __launch_bounds__(64 * W, (T::EB == 2 && KW == 1) ? 3 : 2) void bwd_dkdv_kernel(BwdArgs ba) {
   const AttnArgs& a = ba.f;
   using C_ = ColTile<T, D>;
   constexpr int NK = C_::NK;
@@ -350,7 +386,7 @@ __global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(Bw
 
   int bx, hk, b;
   xcd_order(bx, hk, b);
-  const int key0 = bx * 16 * W;
+  const int key0 = bx * 16 * W * KW;
   const int n = a.seqlens_k[b];
   if (key0 >= n) return;
   const int q0 = a.cu_q[b];
@@ -361,8 +397,6 @@ __global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(Bw
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int G = lane >> 4;
-  const int key = key0 + 16 * wave + (lane & 15);
-  const bool kin = key < n;
 
   // Columns before c_start cannot see key0 (causal); the step grid stays at multiples of 32 from column 0.
   int c_start = 0;
@@ -370,16 +404,23 @@ __global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(Bw
     const int r_min = max(key0 - (n - L), 0);
     c_start = (min(r_min, L) * g) & ~(kBwdCols - 1);
   }
-  // This lane's key is visible to column c (row c / g at position n - L + c / g)
-  // iff c >= c_vis: key <= n - L + floor(c / g)  <=>  c >= (key - n + L) * g.
-  const int c_vis = !kin ? INT_MAX : (a.causal ? max(key - (n - L), 0) * g : 0);
   ColStage<T, D, W> stage;
   if (c_start < ncols) col_stage_load<T, D, W>(ba, q0, hk, ncols, n, L, c_start, stage);
 
-  // This lane's key as the N operand of S and dP: bytes [64k + 16G, +16) of its K and V rows.
-  u32x4 kb[NK], vb[NK];
-  {
-    const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.mbps;
+  // This lane's keys (one per 16-key tile) as the N operand of S and dP: bytes
+  // [64k + 16G, +16) of their K and V rows.  A key is visible to column c (row
+  // c / g at position n - L + c / g) iff c >= c_vis: key <= n - L + floor(c / g)
+  // <=> c >= (key - n + L) * g.
+  int keyv[KW], c_vis[KW];
+  bool kin[KW];
+  u32x4 kb[KW][NK], vb[KW][NK];
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.mbps;
+#pragma unroll
+  for (int kt = 0; kt < KW; ++kt) {
+    const int key = key0 + (wave * KW + kt) * 16 + (lane & 15);
+    keyv[kt] = key;
+    kin[kt] = key < n;
+    c_vis[kt] = !kin[kt] ? INT_MAX : (a.causal ? max(key - (n - L), 0) * g : 0);
     const int kc = min(key, n - 1);
     const int bi = div_block(kc, a.bs_mul, a.bs_shift);
     const int64_t blk = bt[bi];
@@ -388,17 +429,19 @@ __global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(Bw
     const unsigned char* vp = static_cast<const unsigned char*>(a.v) + (blk * a.vbs + slot * a.vss + static_cast<int64_t>(hk) * a.vhs) * T::EB + 16 * G;
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
-      kb[k] = kin ? *reinterpret_cast<const u32x4*>(kp + 64 * k) : u32x4{0, 0, 0, 0};
-      vb[k] = kin ? *reinterpret_cast<const u32x4*>(vp + 64 * k) : u32x4{0, 0, 0, 0};
+      kb[kt][k] = kin[kt] ? *reinterpret_cast<const u32x4*>(kp + 64 * k) : u32x4{0, 0, 0, 0};
+      vb[kt][k] = kin[kt] ? *reinterpret_cast<const u32x4*>(vp + 64 * k) : u32x4{0, 0, 0, 0};
     }
   }
 
-  f32x4 dk[DT], dv[DT];
+  f32x4 dk[KW][DT], dv[KW][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int kt = 0; kt < KW; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dk[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   if (c_start < ncols) col_stage_store<T, D, W>(lds, stage);
   __syncthreads();
@@ -411,52 +454,64 @@ __global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(Bw
     const float* lse_lds = reinterpret_cast<const float*>(q_lds + 2 * C_::BYTES);
     const float* dl_lds = lse_lds + kBwdCols;
 
-    f32x4 s[2], dp[2];
+    f32x4 s[2][KW], dp[2][KW];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       u32x4 x[NK];
       const unsigned char* rq = q_lds + (16 * ct + (lane & 15)) * C_::PITCH + 16 * G;
 #pragma unroll
       for (int k = 0; k < NK; ++k) x[k] = *reinterpret_cast<const u32x4*>(rq + 64 * k);
-      s[ct] = dot_tile<T, NK>(x, kb);
+#pragma unroll
+      for (int kt = 0; kt < KW; ++kt) s[ct][kt] = dot_tile<T, NK>(x, kb[kt]);
       const unsigned char* rd = do_lds + (16 * ct + (lane & 15)) * C_::PITCH + 16 * G;
 #pragma unroll
       for (int k = 0; k < NK; ++k) x[k] = *reinterpret_cast<const u32x4*>(rd + 64 * k);
-      dp[ct] = dot_tile<T, NK>(x, vb);
+#pragma unroll
+      for (int kt = 0; kt < KW; ++kt) dp[ct][kt] = dot_tile<T, NK>(x, vb[kt]);
     }
-    // s[ct][i] and dp[ct][i] at lane l: key l%16 of the wave, column c0 + 16 ct + 4G + i.
-    // When every lane sees the whole step the per-element mask is skipped (it
-    // would select nothing).
-    if (__all(c0 >= c_vis) && c0 + kBwdCols <= ncols) {
+    // s[ct][kt][i], dp[ct][kt][i] at lane l: key tile kt's key l%16, column c0 + 16 ct + 4G + i.
+    // When every lane sees the whole step the per-element mask is skipped (it would select nothing).
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+    for (int kt = 0; kt < KW; ++kt) {
+      if (__all(c0 >= c_vis[kt]) && c0 + kBwdCols <= ncols) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int lc = 16 * ct + 4 * G + i;
-          const float p = pkv_exp<T>(fmaf(s[ct][i], a.mul, -lse_lds[lc]));
-          dp[ct][i] = p * (dp[ct][i] - dl_lds[lc]);  // dS
-          s[ct][i] = p;                              // P
-        }
-    } else {
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+          for (int i = 0; i < 4; ++i) {
+            const int lc = 16 * ct + 4 * G + i;
+            const float p = pkv_exp<T>(fmaf(s[ct][kt][i], a.mul, -lse_lds[lc]));
+            dp[ct][kt][i] = p * (dp[ct][kt][i] - dl_lds[lc]);  // dS
+            s[ct][kt][i] = p;                                  // P
+          }
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int lc = 16 * ct + 4 * G + i;
-          const int c = c0 + lc;
-          const bool vis = c >= c_vis && c < ncols;
-          const float p = vis ? pkv_exp<T>(fmaf(s[ct][i], a.mul, -lse_lds[lc])) : 0.f;
-          dp[ct][i] = vis ? p * (dp[ct][i] - dl_lds[lc]) : 0.f;  // dS
-          s[ct][i] = p;                                         // P
-        }
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int lc = 16 * ct + 4 * G + i;
+            const int c = c0 + lc;
+            const bool vis = c >= c_vis[kt] && c < ncols;
+            const float p = vis ? pkv_exp<T>(fmaf(s[ct][kt][i], a.mul, -lse_lds[lc])) : 0.f;
+            dp[ct][kt][i] = vis ? p * (dp[ct][kt][i] - dl_lds[lc]) : 0.f;  // dS
+            s[ct][kt][i] = p;                                             // P
+          }
+      }
     }
     if constexpr (T::EB == 2) {
-      const u32x4 pp = pack_bf16(s[0], s[1]);
-      const u32x4 pd = pack_bf16(dp[0], dp[1]);
+      u32x4 pp[KW], pd[KW];
+#pragma unroll
+      for (int kt = 0; kt < KW; ++kt) {
+        pp[kt] = pack_bf16(s[0][kt], s[1][kt]);
+        pd[kt] = pack_bf16(dp[0][kt], dp[1][kt]);
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        dv[dt] = mfma_bf16(v_operand_bf16(do_lds, C_::PITCH, 0, dt), pp, dv[dt]);
-        dk[dt] = mfma_bf16(v_operand_bf16(q_lds, C_::PITCH, 0, dt), pd, dk[dt]);
+        const u32x4 xo = v_operand_bf16(do_lds, C_::PITCH, 0, dt);
+#pragma unroll
+        for (int kt = 0; kt < KW; ++kt) dv[kt][dt] = mfma_bf16(xo, pp[kt], dv[kt][dt]);
+        const u32x4 xq = v_operand_bf16(q_lds, C_::PITCH, 0, dt);
+#pragma unroll
+        for (int kt = 0; kt < KW; ++kt) dk[kt][dt] = mfma_bf16(xq, pd[kt], dk[kt][dt]);
       }
     } else {
       // fp32 step (ct, i): k-slot G <-> column 16 ct + 4G + i.
@@ -470,8 +525,11 @@ __global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(Bw
             const int row = 16 * ct + 4 * G + i;
             const float xo = *reinterpret_cast<const float*>(do_lds + row * C_::PITCH + 4 * 16 * dt + dcol);
             const float xq = *reinterpret_cast<const float*>(q_lds + row * C_::PITCH + 4 * 16 * dt + dcol);
-            dv[dt] = mfma_f32(xo, s[ct][i], dv[dt]);
-            dk[dt] = mfma_f32(xq, dp[ct][i], dk[dt]);
+#pragma unroll
+            for (int kt = 0; kt < KW; ++kt) {
+              dv[kt][dt] = mfma_f32(xo, s[ct][kt][i], dv[kt][dt]);
+              dk[kt][dt] = mfma_f32(xq, dp[ct][kt][i], dk[kt][dt]);
+            }
           }
     }
     if (more) col_stage_store<T, D, W>(lds + (cur ^ 1) * BUF, stage);
@@ -479,17 +537,23 @@ __global__ __launch_bounds__(64 * W, T::EB == 2 ? 3 : 2) void bwd_dkdv_kernel(Bw
     cur ^= 1;
   }
 
-  if (kin) {
-    const int64_t kr = (static_cast<int64_t>(ba.cu_k[b]) + key) * (a.hq / g) + hk;
-    store_grad<T, D>(ba.dk, kr * D, dk, ba.scale);
-    store_grad<T, D>(ba.dv, kr * D, dv, 1.0f);
+#pragma unroll
+  for (int kt = 0; kt < KW; ++kt) {
+    if (kin[kt]) {
+      const int64_t kr = (static_cast<int64_t>(ba.cu_k[b]) + keyv[kt]) * (a.hq / g) + hk;
+      store_grad<T, D>(ba.dk, kr * D, dk[kt], ba.scale);
+      store_grad<T, D>(ba.dv, kr * D, dv[kt], 1.0f);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 template <class T, int D>
-static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& pl, hipStream_t stream) {
+static hipError_t launch_bwd_t(const BwdArgs& a_in, const BwdPlan& pl, hipStream_t stream) {
   constexpr int W = 4;
+  constexpr int NT = PKV_DQ_NT;  // column groups per wave of the dq kernel
+  BwdArgs a = a_in;
+  a.f.ncb = static_cast<int>((pl.cols + 16 * W * NT - 1) / (16 * W * NT));
   const int64_t pairs = pl.total_q * a.f.hq;
   if (pairs > 0) {
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(static_cast<unsigned>((pairs + 15) / 16)), dim3(256), 0, stream,
@@ -497,13 +561,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& pl, hipStream_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.f.ncb > 0) {
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, W>), dim3(a.f.ncb, pl.hk, pl.batch), dim3(64 * W), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, NT>), dim3(a.f.ncb, pl.hk, pl.batch), dim3(64 * W), 0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
+  constexpr int KW = (T::EB == 2) ? PKV_DKDV_KW : 1;  // key tiles per wave of the dk/dv kernel
   if (a.nkb > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, W>), dim3(a.nkb, pl.hk, pl.batch), dim3(64 * W), 0, stream, a);
+    a.nkb = static_cast<int>((pl.max_k + 16 * W * KW - 1) / (16 * W * KW));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, W, KW>), dim3(a.nkb, pl.hk, pl.batch), dim3(64 * W), 0, stream, a);
   }
   return hipGetLastError();
 }

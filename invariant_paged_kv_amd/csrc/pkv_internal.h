@@ -117,6 +117,8 @@ struct BwdArgs {
 struct BwdPlan {
   int batch, hk;
   int64_t total_q;
+  int64_t cols;  // max_seqlen_q * (Hq / Hkv): columns per (sequence, KV head)
+  int64_t max_k; // bound on seqlens_k
 };
 
 hipError_t launch_attention(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream);
