@@ -43,6 +43,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #ifndef PKV_ATTN_XCD
 #define PKV_ATTN_XCD 1
 #endif
+#ifndef PKV_QK_PER_MT
+#define PKV_QK_PER_MT 1
+#endif
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND>
 __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
@@ -140,10 +143,14 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
       if constexpr (NT == 1) {
         qk_tile_lds<T, D>(k_lds, q[0], s[0]);  // one M tile of K operands live at a time
       } else {
+#if PKV_QK_PER_MT
+        qk_tiles_lds<T, D, NT>(k_lds, q, s);   // one M tile of K operands, all column groups
+#else
         KOps<T, D> kop;
         k_operands_lds<T, D>(k_lds, kop);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
+#endif
       }
       softmax_pv_tile<T, D, NT>(st, s, lim, j0, a.mul, v_lds);
     }

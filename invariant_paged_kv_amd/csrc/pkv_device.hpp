@@ -259,6 +259,37 @@ __device__ __forceinline__ void qk_tile_lds(const unsigned char* k_lds, const QO
   }
 }
 
+// QK^T of NT column groups with the K operands read from LDS one M tile at a
+// time, each M tile's operands serving every group (the qk_tile chain per group).
+template <class T, int D, int NT>
+__device__ __forceinline__ void qk_tiles_lds(const unsigned char* k_lds, const QOps<T, D> (&q)[NT],
+                                             f32x4 (&s)[NT][KT / 16]) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const unsigned char* base = k_lds + (lane & 15) * G_::KPITCH;
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt) {
+    u32x4 kx[G_::NK];
+#pragma unroll
+    for (int k = 0; k < G_::NK; ++k)
+      kx[k] = *reinterpret_cast<const u32x4*>(base + mt * 16 * G_::KPITCH + qk_piece_off<T>(k, lane >> 4));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < G_::NK; ++k) {
+        if constexpr (T::EB == 2) {
+          acc = mfma_bf16(kx[k], q[nt].v[k], acc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = mfma_f32(__uint_as_float(kx[k][e]), __uint_as_float(q[nt].v[k][e]), acc);
+        }
+      }
+      s[nt][mt] = acc;
+    }
+  }
+}
+
 // V^T operand (A) of PV step ks for d-tile dt, bf16: slot 8G+e <-> key
 // 32ks + 4G + e (e < 4) and 32ks + 16 + 4G + (e - 4) (e >= 4), head-dim row
 // 16dt + l%16.  ds_read_b64_tr_b16 turns four 8-byte row pieces of the 16
