@@ -46,6 +46,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #ifndef PKV_QK_PER_MT
 #define PKV_QK_PER_MT 1
 #endif
+#ifndef PKV_FULL_PIN
+#define PKV_FULL_PIN 1
+#endif
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND>
 __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
         for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
 #endif
       }
-      softmax_pv_tile<T, D, NT>(st, s, lim, j0, a.mul, v_lds);
+      softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {

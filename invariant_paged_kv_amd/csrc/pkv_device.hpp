@@ -32,6 +32,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define PKV_LDS __attribute__((address_space(3)))
+#ifndef PKV_MFMA_PRIO
+#define PKV_MFMA_PRIO 1
+#endif
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -415,6 +418,9 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
   }
 
   if constexpr (T::EB == 2) {
+#if PKV_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
     for (int dt = 0; dt < G_::DT; ++dt) {
 #pragma unroll
@@ -428,6 +434,9 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
       // the arithmetic).
       if constexpr (kPinVReads) __builtin_amdgcn_sched_barrier(0);
     }
+#if PKV_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
   } else {
     // fp32 PV step (mt, i): slot G <-> key 16mt + 4G + i.
     const unsigned char* col = v_lds + 4 * (lane & 15);
