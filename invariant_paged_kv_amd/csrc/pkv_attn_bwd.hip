@@ -52,6 +52,11 @@ __device__ __forceinline__ float elem_f32(const void* p, int64_t i, int eb) {
 #ifndef PKV_DKDV_KW
 #define PKV_DKDV_KW 1
 #endif
+// Raised wave priority over the MFMA blocks that follow the exponentials, so
+// the other wave's VALU work fills the MFMA latency (measured 2-4% faster).
+#ifndef PKV_BWD_PRIO
+#define PKV_BWD_PRIO 1
+#endif
 
 // Work groups are dispatched round-robin over the 8 XCDs (each with its own
 // L2); renumber them so that one XCD runs consecutive blocks of the same
@@ -265,8 +270,11 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
       }
     }
     if constexpr (T::EB == 2) {
+#if PKV_BWD_PRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
-      for (int dt = 0; dt < G_::DT; ++dt)
+      for (int dt = 0; dt < G_::DT; ++dt) {
 #pragma unroll
         for (int ks = 0; ks < KT / 32; ++ks) {
           const u32x4 kt = v_operand_bf16(k_lds, G_::KPITCH, ks, dt);
@@ -274,6 +282,10 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
           for (int nt = 0; nt < NT; ++nt)
             acc[nt][dt] = mfma_bf16(kt, pack_bf16(s[nt][2 * ks], s[nt][2 * ks + 1]), acc[nt][dt]);
         }
+      }
+#if PKV_BWD_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
     } else {
       const unsigned char* colp = k_lds + 4 * (lane & 15);
 #pragma unroll
@@ -504,6 +516,9 @@ __global__ __launch_bounds__(64 * W, (T::EB == 2 && KW == 1) ? 3 : 2) void bwd_d
         pp[kt] = pack_bf16(s[0][kt], s[1][kt]);
         pd[kt] = pack_bf16(dp[0][kt], dp[1][kt]);
       }
+#if PKV_BWD_PRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const u32x4 xo = v_operand_bf16(do_lds, C_::PITCH, 0, dt);
@@ -513,6 +528,9 @@ __global__ __launch_bounds__(64 * W, (T::EB == 2 && KW == 1) ? 3 : 2) void bwd_d
 #pragma unroll
         for (int kt = 0; kt < KW; ++kt) dk[kt][dt] = mfma_bf16(xq, pd[kt], dk[kt][dt]);
       }
+#if PKV_BWD_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
     } else {
       // fp32 step (ct, i): k-slot G <-> column 16 ct + 4G + i.
       const int dcol = 4 * (lane & 15);
