@@ -128,7 +128,7 @@ Plan make_plan(const pkv_layout& l) {
   bool full4 = false;
   if (full && l.dtype != PKV_F32) full4 = g_opt_full_kernel.load() != 1;
   p.lp.full4 = full4;
-  const int cols_per_block = full ? 128 : 16 * waves;
+  const int cols_per_block = full ? 128 : (waves == 1 ? 16 : 16 * 4 * pkv::kSplitGroups);
   p.ncb = static_cast<int>(std::max<int64_t>(1, (cols + cols_per_block - 1) / cols_per_block));
   int64_t cpi = g_opt_split_chunks.load();
   if (cpi <= 0) cpi = 1;
@@ -279,7 +279,8 @@ int run_partials(const void* q, const void* k_cache, const void* v_cache, const 
   a.g = g;
   a.bs = l->block_size;
   a.mbps = l->max_blocks_per_seq;
-  a.ncb = static_cast<int>(std::max<int64_t>(1, (cols + 16 * waves - 1) / (16 * waves)));
+  const int cpb = waves == 1 ? 16 : 16 * 4 * pkv::kSplitGroups;
+  a.ncb = static_cast<int>(std::max<int64_t>(1, (cols + cpb - 1) / cpb));
   a.maxc = max_chunks;
   a.cpi = static_cast<int>(cpi);
   a.chunk0 = c0;

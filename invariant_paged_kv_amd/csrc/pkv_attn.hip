@@ -795,7 +795,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
       hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true, APPEND>), grid, dim3(64), 0, stream, a);
     }
   } else {
-    hipLaunchKernelGGL((attn_kernel<T, D, 4, 1, true, APPEND>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<T, D, 4, kSplitGroups, true, APPEND>), grid, dim3(256), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.skip_merge) return e;

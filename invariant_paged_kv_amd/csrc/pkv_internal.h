@@ -56,6 +56,13 @@ struct MergeArgs {
   int64_t ps_row, ps_chunk;  // partial layout, as in AttnArgs
 };
 
+// Column groups of 16 per wave in the 4-wave split kernel (more than 16
+// columns per KV head): each K/V tile read serves 16 * 4 * kSplitGroups columns.
+#ifndef PKV_SPLIT_NT
+#define PKV_SPLIT_NT 2
+#endif
+constexpr int kSplitGroups = PKV_SPLIT_NT;
+
 struct LaunchPlan {
   bool full;       // prefill kernel (true) or split kernels + merge (false)
   bool full4;      // full path, bf16/FP8: 4 waves x 32 columns (attn_kernel) instead of the 8-wave pipelined kernel
