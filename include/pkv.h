@@ -57,7 +57,7 @@ extern "C" {
 #endif
 
 #define PKV_ABI_VERSION 2
-#define PKV_CHUNK_KEYS 512  /* keys per chunk: the unit partials are merged in */
+#define PKV_CHUNK_KEYS 1024 /* keys per chunk: the unit partials are merged in */
 #define PKV_TILE_KEYS 64    /* keys per tile inside a chunk */
 
 /*

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL = 1, 2, 3
-CHUNK_KEYS = 512
+CHUNK_KEYS = 1024
 TILE_KEYS = 64
 
 # Every symbol include/pkv.h declares.

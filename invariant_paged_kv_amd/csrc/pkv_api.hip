@@ -19,7 +19,7 @@
 namespace {
 
 constexpr int kChunk = PKV_CHUNK_KEYS;
-static_assert(PKV_CHUNK_KEYS == 512 && PKV_TILE_KEYS == 64, "header constants must match the device code");
+static_assert(PKV_CHUNK_KEYS == 1024 && PKV_TILE_KEYS == 64, "header constants must match the device code");
 
 thread_local char g_msg[512] = "";
 std::atomic<int64_t> g_opt_path{0};

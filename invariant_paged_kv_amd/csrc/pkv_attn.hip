@@ -242,17 +242,29 @@ __device__ __forceinline__ void qk_tile_regs(const TileRegs<T, D>& r, const QOps
 
 // Block ids of this lane's four tile rows (rows past jlast use the last
 // visible row's block, so every read stays inside the sequence's blocks).
+// U (block size a multiple of 16): the 16 rows of an M tile lie in one cache
+// block, so its id is wave-uniform and comes from a scalar load -- scalar
+// loads are not counted with the vector loads, so using the ids never makes
+// the wave wait for K/V loads issued before them.
+template <bool U>
 __device__ __forceinline__ void tile_block_ids(const AttnArgs& a, const int32_t* bt, int j0, int jlast,
                                                int (&ids)[KT / 16]) {
-  const int r = lane_id() & 15;
+  if constexpr (U) {
+    using cint = const __attribute__((address_space(4))) int32_t;
+    cint* cbt = (cint*)bt;  // the table is not written while a kernel runs
 #pragma unroll
-  for (int mt = 0; mt < KT / 16; ++mt) {
-    const int j = min(j0 + 16 * mt + r, jlast - 1);
-    ids[mt] = bt[div_block(j, a.bs_mul, a.bs_shift)];
+    for (int mt = 0; mt < KT / 16; ++mt) ids[mt] = cbt[div_block(min(j0 + 16 * mt, jlast - 1), a.bs_mul, a.bs_shift)];
+  } else {
+    const int r = lane_id() & 15;
+#pragma unroll
+    for (int mt = 0; mt < KT / 16; ++mt) {
+      const int j = min(j0 + 16 * mt + r, jlast - 1);
+      ids[mt] = bt[div_block(j, a.bs_mul, a.bs_shift)];
+    }
   }
 }
 
-template <class T, int D, bool APPEND>
+template <class T, int D, bool APPEND, bool U>
 __device__ __forceinline__ void tile_load_regs(const AttnArgs& a, int hk, int j0, int jlast, const int (&ids)[KT / 16],
                                                TileRegs<T, D>& r, bool want_k, bool want_v, const Append& ap) {
   using G_ = TileGeom<T, D>;
@@ -261,56 +273,100 @@ __device__ __forceinline__ void tile_load_regs(const AttnArgs& a, int hk, int j0
   const unsigned char* vb = static_cast<const unsigned char*>(a.v);
 #pragma unroll
   for (int mt = 0; mt < G_::MT; ++mt) {
-    const int j = j0 + 16 * mt + (lane & 15);
-    const bool in = j < jlast;
-    const int jc = min(j, jlast - 1);  // rows past jlast load a visible row, then read as zero
+    // rows past jlast load a visible row; tile_edge zeroes them before use
+    const int jc = min(j0 + 16 * mt + (lane & 15), jlast - 1);
     const int64_t blk = ids[mt];
-    const int64_t slot = jc - div_block(jc, a.bs_mul, a.bs_shift) * a.bs;
+    const int slot = jc - div_block(jc, a.bs_mul, a.bs_shift) * a.bs;
     constexpr int P = kKvPiece<T>;  // stored bytes per 16-byte operand piece
     const int off = P * (lane >> 4);
-    const unsigned char* kp = kb + (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::KVB + off;
-    const unsigned char* vp = vb + (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::KVB + off;
+    const unsigned char* kp;
+    const unsigned char* vp;
+    if constexpr (U) {
+      // wave-uniform block base (scalar registers) + 32-bit per-lane offset
+      const unsigned char* kbase = kb + (blk * a.kbs + (int64_t)hk * a.khs) * T::KVB;
+      const unsigned char* vbase = vb + (blk * a.vbs + (int64_t)hk * a.vhs) * T::KVB;
+      kp = kbase + static_cast<uint32_t>(slot * static_cast<int>(a.kss) * T::KVB + off);
+      vp = vbase + static_cast<uint32_t>(slot * static_cast<int>(a.vss) * T::KVB + off);
+    } else {
+      kp = kb + (blk * a.kbs + (int64_t)slot * a.kss + (int64_t)hk * a.khs) * T::KVB + off;
+      vp = vb + (blk * a.vbs + (int64_t)slot * a.vss + (int64_t)hk * a.vhs) * T::KVB + off;
+    }
     const int nhk = a.hq / a.g;
     const unsigned char* ks = kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kp, off);
     const unsigned char* vs = kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vp, off);
-    using Raw = typename KvRaw<T>::type;
     if constexpr (T::KVB == 1) {
       // FP8: pieces k = 2j and 2j+1 of this lane are 16 contiguous stored bytes
       // at 64j + 16G (the FP8 k-slot map of qk_piece_off).
       const unsigned char* ks2 = ks - off + 16 * (lane >> 4);
       const unsigned char* vs2 = vs - off + 16 * (lane >> 4);
-      const unsigned char* kp2 = kp - off + 16 * (lane >> 4);
-      const unsigned char* vp2 = vp - off + 16 * (lane >> 4);
 #pragma unroll
       for (int j = 0; j < G_::NK / 2; ++j) {
         if (want_k) {
           const u32x4 x = *reinterpret_cast<const u32x4*>(ks2 + 64 * j);
-          kv_store_new<TBf16, APPEND>(ap, in, jc, a.k_store, a.k, kp2 + 64 * j, x);
-          r.k[mt][2 * j] = in ? u32x2{x[0], x[1]} : Raw{};
-          r.k[mt][2 * j + 1] = in ? u32x2{x[2], x[3]} : Raw{};
+          r.k[mt][2 * j] = u32x2{x[0], x[1]};
+          r.k[mt][2 * j + 1] = u32x2{x[2], x[3]};
         }
         if (want_v) {
           const u32x4 x = *reinterpret_cast<const u32x4*>(vs2 + 64 * j);
-          kv_store_new<TBf16, APPEND>(ap, in, jc, a.v_store, a.v, vp2 + 64 * j, x);
-          r.v[mt][2 * j] = in ? u32x2{x[0], x[1]} : Raw{};
-          r.v[mt][2 * j + 1] = in ? u32x2{x[2], x[3]} : Raw{};
+          r.v[mt][2 * j] = u32x2{x[0], x[1]};
+          r.v[mt][2 * j + 1] = u32x2{x[2], x[3]};
         }
       }
       continue;
     }
 #pragma unroll
     for (int k = 0; k < G_::NK; ++k) {
-      if (want_k) {
-        const Raw x = kv_load_raw<T>(ks + 4 * P * k);
-        kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kp + 4 * P * k, x);
-        r.k[mt][k] = in ? x : Raw{};
-      }
-      if (want_v) {
-        const Raw x = kv_load_raw<T>(vs + 4 * P * k);
-        kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vp + 4 * P * k, x);
-        r.v[mt][k] = in ? x : Raw{};
+      if (want_k) r.k[mt][k] = kv_load_raw<T>(ks + 4 * P * k);
+      if (want_v) r.v[mt][k] = kv_load_raw<T>(vs + 4 * P * k);
+    }
+  }
+}
+
+// Rows past jlast hold a copy of row jlast - 1 (tile_load_regs clamps them);
+// zero them when the tile is about to be used rather than when its loads are
+// issued: a select on a loaded register makes the wave wait for that load.
+// Only the last tile of an item can reach past jlast (a wave-uniform test).
+template <class T, int D>
+__device__ __forceinline__ void tile_edge(int j0, int jlast, TileRegs<T, D>& r) {
+  using G_ = TileGeom<T, D>;
+  using Raw = typename KvRaw<T>::type;
+  if (j0 + KT > jlast) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int mt = 0; mt < G_::MT; ++mt) {
+      const bool in = j0 + 16 * mt + (lane & 15) < jlast;
+#pragma unroll
+      for (int k = 0; k < G_::NK; ++k) {
+        r.k[mt][k] = in ? r.k[mt][k] : Raw{};
+        r.v[mt][k] = in ? r.v[mt][k] : Raw{};
       }
     }
+  }
+}
+
+// Fused append in the split kernels: the writer copies this call's new rows
+// in [lo, hi) (positions >= n_old) of KV head hk from k_new / v_new into
+// their cache slots once, before its tile loop.  Every read of those rows in
+// this call goes to k_new / v_new (kv_src), so the copy's position in the
+// kernel does not matter, and the tile loop carries no stores.
+template <class T, int D>
+__device__ __forceinline__ void append_rows(const AttnArgs& a, const int32_t* bt, int hk, int lo, int hi,
+                                            const Append& ap) {
+  constexpr int PR = D * T::KVB / 16;  // 16-byte pieces per stored row
+  const int nhk = a.hq / a.g;
+  for (int i = lane_id(); i < (hi - lo) * PR; i += 64) {
+    const int j = lo + i / PR;
+    const int p = i % PR;
+    const int bi = div_block(j, a.bs_mul, a.bs_shift);
+    const int64_t blk = bt[bi];
+    const int64_t slot = j - bi * a.bs;
+    const int64_t nrow = (ap.row0 + (j - ap.n_old)) * nhk + hk;
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(a.k_new) + nrow * D * T::KVB + 16 * p);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(a.v_new) + nrow * D * T::KVB + 16 * p);
+    *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.k_store) +
+                              (blk * a.kbs + slot * a.kss + (int64_t)hk * a.khs) * T::KVB + 16 * p) = kx;
+    *reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.v_store) +
+                              (blk * a.vbs + slot * a.vss + (int64_t)hk * a.vhs) * T::KVB + 16 * p) = vx;
   }
 }
 
@@ -510,7 +566,7 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
 
 // Two waves per SIMD (<= 256 registers): 8 waves per CU, each with one tile
 // (32 KiB at d = 128) of K/V loads in flight while it computes the previous one.
-template <class T, int D, bool APPEND>
+template <class T, int D, bool APPEND, bool U>
 __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
@@ -555,12 +611,19 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   }
 
   const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
+  if constexpr (APPEND) {
+    if (ap.writer) append_rows<T, D>(a, bt, hk, max(ap.n_old, c_begin * KC), jlast, ap);
+  }
   int j0 = c_begin * KC;
   int ids[KT / 16];
   TileRegs<T, D> r;
-  tile_block_ids(a, bt, j0, jlast, ids);
-  tile_load_regs<T, D, APPEND>(a, hk, j0, jlast, ids, r, true, true, ap);
-  tile_block_ids(a, bt, j0 + KT, jlast, ids);
+  tile_block_ids<U>(a, bt, j0, jlast, ids);
+  // V then K, the order the loop issues them in (see below)
+  tile_load_regs<T, D, APPEND, U>(a, hk, j0, jlast, ids, r, false, true, ap);
+  __builtin_amdgcn_sched_barrier(0);
+  tile_load_regs<T, D, APPEND, U>(a, hk, j0, jlast, ids, r, true, false, ap);
+  tile_block_ids<U>(a, bt, j0 + KT, jlast, ids);
+  __builtin_amdgcn_sched_barrier(0);
 
   // Per tile: copy V(t) to LDS and refill those registers with V(t+1); QK on
   // K(t) and refill with K(t+1); then softmax + PV(t) while t+1 is in flight.
@@ -569,16 +632,22 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
     chunk_reset(st);
     const int jend = min((c + 1) * KC, jmax);
     for (; j0 < jend; j0 += KT) {
+      // The next tile's loads are issued unconditionally: past the item's
+      // last key every row clamps to row jlast - 1 (a cache hit), and a load
+      // under a branch would make the compiler wait for all loads in flight
+      // where the branch rejoins.
       const int jn = j0 + KT;
-      const bool more = jn < jlast;
+      tile_edge<T, D>(j0, jlast, r);
       tile_store_v<T, D>(v_lds, r);
-      if (more) tile_load_regs<T, D, APPEND>(a, hk, jn, jlast, ids, r, false, true, ap);
+      tile_load_regs<T, D, APPEND, U>(a, hk, jn, jlast, ids, r, false, true, ap);
+      // Loads complete in issue order: keep all of V(t+1) ahead of K(t+1), so
+      // waiting for V(t+1) at the next tile leaves K(t+1) in flight.
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 s[1][KT / 16];
       qk_tile_regs<T, D>(r, q, s[0]);
-      if (more) {
-        tile_load_regs<T, D, APPEND>(a, hk, jn, jlast, ids, r, true, false, ap);
-        tile_block_ids(a, bt, jn + KT, jlast, ids);
-      }
+      tile_load_regs<T, D, APPEND, U>(a, hk, jn, jlast, ids, r, true, false, ap);
+      tile_block_ids<U>(a, bt, jn + KT, jlast, ids);
+      __builtin_amdgcn_sched_barrier(0);
       softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
     }
     const float lc = column_sum(st.l[0]);
@@ -602,20 +671,29 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
 // tile t+2) -- the same 32 KiB of HBM reads per wave as the bf16 kernel with
 // one tile ahead.  Same chunk core and partial writes as decode_kernel.
 // ---------------------------------------------------------------------------
-template <class T, int D, bool APPEND>
+template <class T, int D, bool APPEND, bool U>
 __device__ __forceinline__ void decode2_tile(const AttnArgs& a, const int32_t* bt, int hk, int t, int t_end, int jlast,
                                              int (&ids)[KT / 16], TileRegs<T, D>& r, unsigned char* v_lds,
                                              const QOps<T, D>& q, const int (&lim)[1], ChunkState<D, 1>& st,
                                              const Append& ap, bool col_ok, int64_t part_row) {
   constexpr int TPC = KC / KT;  // tiles per chunk
   const int j0 = t * KT;
-  tile_store_v<T, D>(v_lds, r);
+  // Tile t exists unless it is the odd tile after the item's last one; the
+  // loads below are issued either way, so every pass through the loop issues
+  // the same loads in the same order and the waits for a stage's tile never
+  // include the other stage's loads.
+  const bool valid = t < t_end;
   f32x4 s[1][KT / 16];
-  qk_tile_regs<T, D>(r, q, s[0]);
-  if (t + 2 < t_end) {
-    tile_load_regs<T, D, APPEND>(a, hk, j0 + 2 * KT, jlast, ids, r, true, true, ap);
-    tile_block_ids(a, bt, j0 + 3 * KT, jlast, ids);
+  if (valid) {
+    tile_edge<T, D>(j0, jlast, r);
+    tile_store_v<T, D>(v_lds, r);
+    qk_tile_regs<T, D>(r, q, s[0]);
   }
+  // past jlast the rows clamp to jlast - 1 (a cache hit); ids (this register
+  // stage's own) then move on to tile t+4
+  tile_load_regs<T, D, APPEND, U>(a, hk, j0 + 2 * KT, jlast, ids, r, true, true, ap);
+  tile_block_ids<U>(a, bt, j0 + 4 * KT, jlast, ids);
+  if (!valid) return;
   softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
   if ((t + 1) % TPC == 0 || t + 1 == t_end) {
     const float lc = column_sum(st.l[0]);
@@ -633,7 +711,7 @@ __device__ __forceinline__ void decode2_tile(const AttnArgs& a, const int32_t* b
   }
 }
 
-template <class T, int D, bool APPEND>
+template <class T, int D, bool APPEND, bool U>
 __global__ __launch_bounds__(64, 2) void decode2_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
@@ -675,24 +753,30 @@ __global__ __launch_bounds__(64, 2) void decode2_kernel(AttnArgs a) {
   const int64_t part_row = (int64_t)(q0 + col / g) * a.hq + hk * g + col % g;
 
   const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
+  if constexpr (APPEND) {
+    if (ap.writer) append_rows<T, D>(a, bt, hk, max(ap.n_old, c_begin * KC), jlast, ap);
+  }
   const int t_begin = c_begin * (KC / KT);
   const int t_end = (jlast + KT - 1) / KT;
-  int ids[KT / 16];
+  int ida[KT / 16], idb[KT / 16];  // block ids of the next tile of each register stage
   TileRegs<T, D> ra, rb;
-  tile_block_ids(a, bt, t_begin * KT, jlast, ids);
-  tile_load_regs<T, D, APPEND>(a, hk, t_begin * KT, jlast, ids, ra, true, true, ap);
-  if (t_begin + 1 < t_end) {
-    tile_block_ids(a, bt, (t_begin + 1) * KT, jlast, ids);
-    tile_load_regs<T, D, APPEND>(a, hk, (t_begin + 1) * KT, jlast, ids, rb, true, true, ap);
-  }
-  tile_block_ids(a, bt, (t_begin + 2) * KT, jlast, ids);
+  // The prologue leaves the loads in the loop's steady-state order (stage a's
+  // tile and ids, then stage b's), so the waits at the top of the loop are the
+  // same on the first and on every later pass.
+  tile_block_ids<U>(a, bt, t_begin * KT, jlast, ida);
+  tile_block_ids<U>(a, bt, (t_begin + 1) * KT, jlast, idb);
+  tile_load_regs<T, D, APPEND, U>(a, hk, t_begin * KT, jlast, ida, ra, true, true, ap);
+  tile_block_ids<U>(a, bt, (t_begin + 2) * KT, jlast, ida);
+  __builtin_amdgcn_sched_barrier(0);
+  tile_load_regs<T, D, APPEND, U>(a, hk, (t_begin + 1) * KT, jlast, idb, rb, true, true, ap);
+  tile_block_ids<U>(a, bt, (t_begin + 3) * KT, jlast, idb);
+  __builtin_amdgcn_sched_barrier(0);
 
   ChunkState<D, 1> st;
   chunk_reset(st);
   for (int t = t_begin; t < t_end; t += 2) {
-    decode2_tile<T, D, APPEND>(a, bt, hk, t, t_end, jlast, ids, ra, v_lds, q, lim, st, ap, col < ncols, part_row);
-    if (t + 1 < t_end)
-      decode2_tile<T, D, APPEND>(a, bt, hk, t + 1, t_end, jlast, ids, rb, v_lds, q, lim, st, ap, col < ncols, part_row);
+    decode2_tile<T, D, APPEND, U>(a, bt, hk, t, t_end, jlast, ida, ra, v_lds, q, lim, st, ap, col < ncols, part_row);
+    decode2_tile<T, D, APPEND, U>(a, bt, hk, t + 1, t_end, jlast, idb, rb, v_lds, q, lim, st, ap, col < ncols, part_row);
   }
 }
 
@@ -787,10 +871,20 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   }
   dim3 grid(a.ncb * pl.items, pl.hk, pl.batch);
   if (pl.waves == 1) {
+    // Uniform block ids per 16-row M tile (block size a multiple of 16) with
+    // 32-bit in-block offsets: scalar id loads and scalar-based addresses.
+    const int64_t span = (static_cast<int64_t>(a.bs) - 1) * std::max(a.kss, a.vss) * T::KVB + D * T::KVB;
+    const bool uni = a.bs % 16 == 0 && a.kss >= 0 && a.vss >= 0 && span < (int64_t{1} << 31);
     if constexpr (T::KVB == 1) {
-      hipLaunchKernelGGL((decode2_kernel<T, D, APPEND>), grid, dim3(64), 0, stream, a);
+      if (uni)
+        hipLaunchKernelGGL((decode2_kernel<T, D, APPEND, true>), grid, dim3(64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode2_kernel<T, D, APPEND, false>), grid, dim3(64), 0, stream, a);
     } else if constexpr (T::EB == 2) {
-      hipLaunchKernelGGL((decode_kernel<T, D, APPEND>), grid, dim3(64), 0, stream, a);
+      if (uni)
+        hipLaunchKernelGGL((decode_kernel<T, D, APPEND, true>), grid, dim3(64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_kernel<T, D, APPEND, false>), grid, dim3(64), 0, stream, a);
     } else {
       hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true, APPEND>), grid, dim3(64), 0, stream, a);
     }

@@ -21,7 +21,7 @@
 namespace pkv {
 
 constexpr int KT = 64;   // keys per tile (online-softmax step inside a chunk)
-constexpr int KC = 512;  // keys per chunk (unit of split partials and of the fold)
+constexpr int KC = 1024;  // keys per chunk (unit of split partials and of the fold)
 static_assert(KC % KT == 0, "a chunk is a whole number of tiles");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -98,10 +98,10 @@ def test_append_decode_rows(layout, bs):
 
 
 def test_append_chunk_rows_cross_chunk_boundary():
-    """17 new rows straddling a 512-key chunk boundary, several KV heads per column block."""
+    """17 new rows straddling a chunk boundary (1024 and 2048 keys), several KV heads per column block."""
     announce("append 17 rows across a chunk boundary")
     check_same(dict(seed=5100, hq=16, hk=4, d=128, bs=16, layout="interleaved",
-                    seqlens=[520, 1041], lens=[17, 17]))
+                    seqlens=[1030, 2060], lens=[17, 17]))
 
 
 def test_append_long_prefill_rows():
