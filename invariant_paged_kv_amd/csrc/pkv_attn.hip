@@ -50,7 +50,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #define PKV_FULL_PIN 1
 #endif
 
-template <class T, int D, int W, int NT, bool SPLIT, bool APPEND>
+template <class T, int D, int W, int NT, bool SPLIT, bool APPEND, bool U>
 __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   constexpr int COLS = W * NT * 16;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
     const int jend = min((c + 1) * KC, jmax);
     for (int j0 = c * KC; j0 < jend; j0 += KT) {
       __syncthreads();
-      load_tile<T, D, W, APPEND>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
+      load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
       __syncthreads();
       f32x4 s[NT][KT / 16];
       if constexpr (NT == 1) {
@@ -856,25 +856,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 // ---------------------------------------------------------------------------
 template <class T, int D, bool APPEND>
 static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStream_t stream) {
+  // Uniform block ids per 16 rows (block size a multiple of 16) with 32-bit
+  // in-block offsets: scalar id loads and scalar-based addresses.
+  const int64_t span = (static_cast<int64_t>(a.bs) - 1) * std::max(a.kss, a.vss) * T::KVB + D * T::KVB;
+  const bool uni = a.bs % 16 == 0 && a.kss >= 0 && a.vss >= 0 && span < (int64_t{1} << 31);
   if (pl.full) {
     dim3 grid(a.ncb, pl.hk, pl.batch);
-    if constexpr (T::EB == 2) {
-      if (pl.full4) {
-        hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false, APPEND>), grid, dim3(256), 0, stream, a);
-      } else {
-        hipLaunchKernelGGL((prefill_kernel<T, D, 8, APPEND>), grid, dim3(512), 0, stream, a);
-      }
+    if (T::EB == 2 && !pl.full4) {
+      if constexpr (T::EB == 2) hipLaunchKernelGGL((prefill_kernel<T, D, 8, APPEND>), grid, dim3(512), 0, stream, a);
+    } else if (uni) {
+      hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false, APPEND, true>), grid, dim3(256), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false, APPEND>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 4, 2, false, APPEND, false>), grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();
   }
   dim3 grid(a.ncb * pl.items, pl.hk, pl.batch);
   if (pl.waves == 1) {
-    // Uniform block ids per 16-row M tile (block size a multiple of 16) with
-    // 32-bit in-block offsets: scalar id loads and scalar-based addresses.
-    const int64_t span = (static_cast<int64_t>(a.bs) - 1) * std::max(a.kss, a.vss) * T::KVB + D * T::KVB;
-    const bool uni = a.bs % 16 == 0 && a.kss >= 0 && a.vss >= 0 && span < (int64_t{1} << 31);
     if constexpr (T::KVB == 1) {
       if (uni)
         hipLaunchKernelGGL((decode2_kernel<T, D, APPEND, true>), grid, dim3(64), 0, stream, a);
@@ -886,10 +884,12 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
       else
         hipLaunchKernelGGL((decode_kernel<T, D, APPEND, false>), grid, dim3(64), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true, APPEND>), grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true, APPEND, false>), grid, dim3(64), 0, stream, a);
     }
+  } else if (uni) {
+    hipLaunchKernelGGL((attn_kernel<T, D, 4, kSplitGroups, true, APPEND, true>), grid, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attn_kernel<T, D, 4, kSplitGroups, true, APPEND>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<T, D, 4, kSplitGroups, true, APPEND, false>), grid, dim3(256), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.skip_merge) return e;

@@ -61,7 +61,12 @@ __device__ __forceinline__ void kv_store_new(const Append& ap, bool in, int jc, 
 // key row (16 stored bytes, or 8 FP8 bytes widened to 16).  The block address
 // uses the real block stride (contiguous or K/V-interleaved caches alike).
 // Keys >= jmax are not read; their rows are zero.
-template <class T, int D, int W, bool APPEND>
+// U (block size a multiple of 16, in-block offsets below 2^31 bytes): the rows
+// one wave loads with one instruction lie in one 16-row group, hence in one
+// cache block; its id is a scalar load and the address a scalar block base
+// plus a 32-bit lane offset, instead of a per-lane table lookup and 64-bit
+// address arithmetic for every piece.
+template <class T, int D, int W, bool APPEND, bool U = false>
 __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
                                           unsigned char* k_lds, unsigned char* v_lds, const Append& ap) {
   using G_ = TileGeom<T, D>;
@@ -80,12 +85,29 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
       const int row = qi / G_::CPR, part = qi % G_::CPR;
       const int j = j0 + row;
       const int jc = min(j, jmax - 1);  // rows past jmax load a visible row, then read as zero
-      const int bi = div_block(jc, a.bs_mul, a.bs_shift);
-      const int64_t blk = bt[bi];
-      const int64_t slot = jc - bi * a.bs;
       const int off = kKvPiece<T> * part;
-      const unsigned char* kc = kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::KVB + off;
-      const unsigned char* vc = vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::KVB + off;
+      const unsigned char* kc;
+      const unsigned char* vc;
+      if constexpr (U) {
+        static_assert(64 % G_::CPR == 0 && 64 / G_::CPR <= 16, "a wave's rows must lie in one 16-row group");
+        // Clamped rows stay in their group's block: a group holds rows past
+        // jmax only if jmax - 1 is in it, or the whole group clamps to it.
+        const int g0 = __builtin_amdgcn_readfirstlane(row) & ~15;
+        const int bi = div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift);
+        using cint = const __attribute__((address_space(4))) int32_t;
+        const int64_t blk = ((cint*)bt)[bi];  // the table is not written while a kernel runs
+        const int slot = jc - bi * a.bs;
+        kc = kb + (blk * a.kbs + (int64_t)hk * a.khs) * T::KVB +
+             static_cast<uint32_t>(slot * static_cast<int>(a.kss) * T::KVB + off);
+        vc = vb + (blk * a.vbs + (int64_t)hk * a.vhs) * T::KVB +
+             static_cast<uint32_t>(slot * static_cast<int>(a.vss) * T::KVB + off);
+      } else {
+        const int bi = div_block(jc, a.bs_mul, a.bs_shift);
+        const int64_t blk = bt[bi];
+        const int64_t slot = jc - bi * a.bs;
+        kc = kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::KVB + off;
+        vc = vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::KVB + off;
+      }
       const int nhk = a.hq / a.g;
       const auto kv = kv_load_raw<T>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, off));
       const auto vv = kv_load_raw<T>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, off));
