@@ -32,11 +32,25 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_c5_traffic.json")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def settle(torch, fn, min_ms: float = 200.0, min_calls: int = 3):
+    """Untimed calls of fn until at least min_calls calls and min_ms of wall time
+    have passed, so the GPU clocks have settled before a timed region."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_calls or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
@@ -180,14 +194,13 @@ def main():
         return pkv.attn_forward(q_rs, pool.k, pool.v, bt, seqlens, cu_rs, True, scale, max_seqlen_q=RS,
                                 max_seqlen_k=N)
 
-    rescore()
-    torch.cuda.synchronize()
+    settle(torch, rescore)
     ev0.record(stream)
-    for _ in range(3):
+    for _ in range(5):
         rescore()
     ev1.record(stream)
     ev1.synchronize()
-    rs_ms = ev0.elapsed_time(ev1) / 3
+    rs_ms = ev0.elapsed_time(ev1) / 5
     rs_flops = 4.0 * D * HQ * B * sum(N - RS + 1 + r for r in range(RS))
     result["rescore_prefill"] = {"workload": "64-row causal prefill per sequence over the same 131072-key cache",
                                  "ms": round(rs_ms, 3), "tflops": round(rs_flops / (rs_ms * 1e-3) / 1e12, 2),
@@ -280,7 +293,7 @@ def bench_fp8_decode(torch, pkv, gen, B, N, steps, warmup, bf16_ms):
             "speedup_vs_bf16_call": round(bf16_ms / ms, 3), "bitwise_decode_eq_prefill_kernel": same}
 
 
-def bench_prefill(torch, pkv, gen, reps: int = 3):
+def bench_prefill(torch, pkv, gen, reps: int = 5):
     """Full causal prefill, batch 8 x 8192 tokens, Hq 16, Hkv 4, d 128, bs 16 (TFLOP/s of causal pairs)."""
     dev = "cuda"
     B, HQ, HK, D, BS, S = 8, 16, 4, 128, 16, 8192
@@ -296,8 +309,7 @@ def bench_prefill(torch, pkv, gen, reps: int = 3):
     def call():
         return pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu, True, scale, max_seqlen_q=S, max_seqlen_k=S)
 
-    call()
-    torch.cuda.synchronize()
+    settle(torch, call)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -326,8 +338,7 @@ def bench_prefill(torch, pkv, gen, reps: int = 3):
         return pkv.attn_backward(q, pool.k, pool.v, bt, sk, cu, True, scale, out, lse, dout, max_seqlen_q=S,
                                  max_seqlen_k=S, cu_seqlens_k=cuk, total_k=B * S, dq=dq, dk=dk, dv=dv)
 
-    bwd()
-    torch.cuda.synchronize()
+    settle(torch, bwd)
     e0.record()
     for _ in range(reps):
         bwd()

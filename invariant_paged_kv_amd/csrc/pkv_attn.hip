@@ -49,6 +49,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #ifndef PKV_FULL_PIN
 #define PKV_FULL_PIN 1
 #endif
+#ifndef PKV_FULL_PREFETCH
+#define PKV_FULL_PREFETCH 1
+#endif
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND, bool U>
 __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
@@ -134,13 +137,25 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   }
 
   const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
+  // bf16/FP8 with 4 waves: the next tile's loads are issued between the
+  // softmax and the P.V products of the current one (into registers the
+  // scores have freed) and written to LDS after the next barrier; fp32 and
+  // the fused-append variant (whose store of the new rows would spill) load
+  // each tile when it starts.  Past the item's last tile the rows clamp to
+  // jmax - 1, so the extra issue stays in bounds.
+  constexpr bool kPrefetch = PKV_FULL_PREFETCH && T::EB == 2 && W == 4 && !APPEND;
+  TileStage<T, D, W> stg;
+  if constexpr (kPrefetch) tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC, jmax, stg, ap);
   ChunkState<D, NT> st;
   for (int c = c_begin; c < c_end; ++c) {
     chunk_reset(st);
     const int jend = min((c + 1) * KC, jmax);
     for (int j0 = c * KC; j0 < jend; j0 += KT) {
       __syncthreads();
-      load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
+      if constexpr (kPrefetch)
+        tile_commit<T, D, W, APPEND>(a, bt, hk, j0, jmax, stg, k_lds, v_lds, ap);
+      else
+        load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
       __syncthreads();
       f32x4 s[NT][KT / 16];
       if constexpr (NT == 1) {
@@ -155,7 +170,12 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
         for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
 #endif
       }
-      softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
+      if constexpr (kPrefetch) {
+        softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(
+            st, s, lim, j0, a.mul, v_lds, [&] { tile_issue<T, D, W, APPEND, U>(a, bt, hk, j0 + KT, jmax, stg, ap); });
+      } else {
+        softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
+      }
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {

@@ -345,10 +345,16 @@ __device__ __forceinline__ u32x4 v_operand_bf16(const unsigned char* v_lds, int 
 // tile the per-key mask is skipped (kShortcuts; it would select nothing), and
 // when every column's alpha is exactly 1 the multiply of o is skipped.
 // ---------------------------------------------------------------------------
-template <class T, int D, int NT, bool kPinVReads = false, bool kShortcuts = true>
+struct NoMid {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// `mid` runs between the softmax and the P.V products (the full-path kernels
+// issue the next tile's loads there, into registers the scores no longer use).
+template <class T, int D, int NT, bool kPinVReads = false, bool kShortcuts = true, class Mid = NoMid>
 __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
                                                 const int (&lim)[NT], int j0, float mul,
-                                                const unsigned char* v_lds) {
+                                                const unsigned char* v_lds, const Mid& mid = Mid{}) {
   using G_ = TileGeom<T, D>;
   const int lane = lane_id();
   const int G = lane >> 4;
@@ -417,6 +423,7 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
     }
   }
 
+  mid();
   if constexpr (T::EB == 2) {
 #if PKV_MFMA_PRIO
     __builtin_amdgcn_s_setprio(1);

@@ -78,6 +78,26 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
   const unsigned char* vb = static_cast<const unsigned char*>(a.v);
 #pragma unroll
   for (int r0 = 0; r0 < PER; r0 += R) {
+    // U: the block ids of this wave's row groups, all scalar loads issued
+    // before any of them is used.  Clamped rows stay in their group's block:
+    // a group holds rows past jmax only if jmax - 1 is in it, or the whole
+    // group clamps to it.
+    // Unsigned (block ids are non-negative): widening it needs no instruction,
+    // whereas a sign extension next to the load would wait for the load.
+    uint32_t ublk[R];
+    int ubase[R];
+    if constexpr (U) {
+      static_assert(64 % G_::CPR == 0 && 64 / G_::CPR <= 16, "a wave's rows must lie in one 16-row group");
+      using cint = const __attribute__((address_space(4))) int32_t;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int row = (threadIdx.x + (r0 + i) * 64 * W) / G_::CPR;
+        const int g0 = __builtin_amdgcn_readfirstlane(row) & ~15;
+        const int bi = div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift);
+        ublk[i] = static_cast<uint32_t>(((cint*)bt)[bi]);  // the table is not written while a kernel runs
+        ubase[i] = bi * a.bs;
+      }
+    }
     u32x4 kr[R], vr[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -89,14 +109,8 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
       const unsigned char* kc;
       const unsigned char* vc;
       if constexpr (U) {
-        static_assert(64 % G_::CPR == 0 && 64 / G_::CPR <= 16, "a wave's rows must lie in one 16-row group");
-        // Clamped rows stay in their group's block: a group holds rows past
-        // jmax only if jmax - 1 is in it, or the whole group clamps to it.
-        const int g0 = __builtin_amdgcn_readfirstlane(row) & ~15;
-        const int bi = div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift);
-        using cint = const __attribute__((address_space(4))) int32_t;
-        const int64_t blk = ((cint*)bt)[bi];  // the table is not written while a kernel runs
-        const int slot = jc - bi * a.bs;
+        const int slot = jc - ubase[i];
+        const int64_t blk = static_cast<int64_t>(static_cast<uint64_t>(ublk[i]));
         kc = kb + (blk * a.kbs + (int64_t)hk * a.khs) * T::KVB +
              static_cast<uint32_t>(slot * static_cast<int>(a.kss) * T::KVB + off);
         vc = vb + (blk * a.vbs + (int64_t)hk * a.vhs) * T::KVB +
@@ -114,8 +128,19 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
       const bool in = j < jmax;
       kv_store_new<T, APPEND>(ap, in, jc, a.k_store, a.k, kc, kv);
       kv_store_new<T, APPEND>(ap, in, jc, a.v_store, a.v, vc, vv);
-      kr[i] = in ? kv_widen<T>(kv) : u32x4{0, 0, 0, 0};
-      vr[i] = in ? kv_widen<T>(vv) : u32x4{0, 0, 0, 0};
+      kr[i] = kv_widen<T>(kv);
+      vr[i] = kv_widen<T>(vv);
+    }
+    // rows past jmax read as zero; only a tile reaching past jmax has any
+    if (j0 + KT > jmax) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int row = (threadIdx.x + (r0 + i) * 64 * W) / G_::CPR;
+        if (j0 + row >= jmax) {
+          kr[i] = u32x4{0, 0, 0, 0};
+          vr[i] = u32x4{0, 0, 0, 0};
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -124,6 +149,118 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt, 
       *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = kr[i];
       *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = vr[i];
     }
+  }
+}
+
+// The same tile load split in two, so the loads can be in flight while the
+// previous tile is computed: tile_issue loads a tile's stored bytes into a
+// register stage (nothing waits for them there); tile_commit, after the
+// barrier that frees the LDS tile, widens them, zeroes rows past jmax, does
+// the fused-append store and writes the LDS tile.  Same bytes, same LDS
+// layout as load_tile.
+template <class T, int D, int W>
+struct TileStage {
+  static constexpr int PER = KT * TileGeom<T, D>::CPR / (64 * W);
+  typename KvRaw<T>::type k[PER], v[PER];
+};
+
+template <class T, int D, int W, bool APPEND, bool U>
+__device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
+                                           TileStage<T, D, W>& stg, const Append& ap) {
+  using G_ = TileGeom<T, D>;
+  constexpr int PER = TileStage<T, D, W>::PER;
+  const unsigned char* kb = static_cast<const unsigned char*>(a.k);
+  const unsigned char* vb = static_cast<const unsigned char*>(a.v);
+  uint32_t ublk[PER];  // U: block ids of the wave's row groups (see load_tile)
+  int ubase[PER];
+  if constexpr (U) {
+    static_assert(64 % G_::CPR == 0 && 64 / G_::CPR <= 16, "a wave's rows must lie in one 16-row group");
+    using cint = const __attribute__((address_space(4))) int32_t;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int row = (threadIdx.x + i * 64 * W) / G_::CPR;
+      const int g0 = __builtin_amdgcn_readfirstlane(row) & ~15;
+      const int bi = div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift);
+      ublk[i] = static_cast<uint32_t>(((cint*)bt)[bi]);
+      ubase[i] = bi * a.bs;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int qi = threadIdx.x + i * 64 * W;
+    const int row = qi / G_::CPR, part = qi % G_::CPR;
+    const int jc = min(j0 + row, jmax - 1);
+    const int off = kKvPiece<T> * part;
+    const unsigned char* kc;
+    const unsigned char* vc;
+    if constexpr (U) {
+      const int slot = jc - ubase[i];
+      const int64_t blk = static_cast<int64_t>(static_cast<uint64_t>(ublk[i]));
+      kc = kb + (blk * a.kbs + (int64_t)hk * a.khs) * T::KVB +
+           static_cast<uint32_t>(slot * static_cast<int>(a.kss) * T::KVB + off);
+      vc = vb + (blk * a.vbs + (int64_t)hk * a.vhs) * T::KVB +
+           static_cast<uint32_t>(slot * static_cast<int>(a.vss) * T::KVB + off);
+    } else {
+      const int bi = div_block(jc, a.bs_mul, a.bs_shift);
+      const int64_t blk = bt[bi];
+      const int64_t slot = jc - bi * a.bs;
+      kc = kb + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::KVB + off;
+      vc = vb + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::KVB + off;
+    }
+    const int nhk = a.hq / a.g;
+    stg.k[i] = kv_load_raw<T>(kv_src<T, D, APPEND>(a.k_new, nhk, hk, jc, ap, kc, off));
+    stg.v[i] = kv_load_raw<T>(kv_src<T, D, APPEND>(a.v_new, nhk, hk, jc, ap, vc, off));
+  }
+}
+
+template <class T, int D, int W, bool APPEND>
+__device__ __forceinline__ void tile_commit(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
+                                            const TileStage<T, D, W>& stg, unsigned char* k_lds,
+                                            unsigned char* v_lds, const Append& ap) {
+  using G_ = TileGeom<T, D>;
+  constexpr int PER = TileStage<T, D, W>::PER;
+  if constexpr (APPEND) {
+    // the writer stores this call's new rows (only the tiles reaching them)
+    if (ap.writer && j0 + KT > ap.n_old) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int qi = threadIdx.x + i * 64 * W;
+        const int row = qi / G_::CPR, part = qi % G_::CPR;
+        const int j = j0 + row;
+        const int jc = min(j, jmax - 1);
+        const int bi = div_block(jc, a.bs_mul, a.bs_shift);
+        const int64_t blk = bt[bi];
+        const int64_t slot = jc - bi * a.bs;
+        const int off = kKvPiece<T> * part;
+        const unsigned char* kc = static_cast<const unsigned char*>(a.k) + (blk * a.kbs + slot * a.kss + hk * a.khs) * T::KVB + off;
+        const unsigned char* vc = static_cast<const unsigned char*>(a.v) + (blk * a.vbs + slot * a.vss + hk * a.vhs) * T::KVB + off;
+        kv_store_new<T, APPEND>(ap, j < jmax, jc, a.k_store, a.k, kc, stg.k[i]);
+        kv_store_new<T, APPEND>(ap, j < jmax, jc, a.v_store, a.v, vc, stg.v[i]);
+      }
+    }
+  }
+  u32x4 kr[PER], vr[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    kr[i] = kv_widen<T>(stg.k[i]);
+    vr[i] = kv_widen<T>(stg.v[i]);
+  }
+  if (j0 + KT > jmax) {  // rows past jmax read as zero
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int row = (threadIdx.x + i * 64 * W) / G_::CPR;
+      if (j0 + row >= jmax) {
+        kr[i] = u32x4{0, 0, 0, 0};
+        vr[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int qi = threadIdx.x + i * 64 * W;
+    const int row = qi / G_::CPR, part = qi % G_::CPR;
+    *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = kr[i];
+    *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = vr[i];
   }
 }
 
