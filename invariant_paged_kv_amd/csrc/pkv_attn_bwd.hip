@@ -177,7 +177,7 @@ __device__ __forceinline__ void row_operands_global(const void* base, int64_t ro
 //   P = exp(S * mul - lse), dS = P (dP - delta) (0 for invisible keys),
 //   dQ^T += K^T dS^T (head dim as M, keys as the k-dimension, as the forward's PV).
 // ---------------------------------------------------------------------------
-template <class T, int D, int W, int NT>
+template <class T, int D, int W, int NT, bool U>
 __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
   const AttnArgs& a = ba.f;
   using G_ = TileGeom<T, D>;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
   const Append none;
   for (int j0 = 0; j0 < jmax; j0 += KT) {
     __syncthreads();
-    load_tile<T, D, W, false>(a, bt, hk, j0, jmax, k_lds, v_lds, none);
+    load_tile<T, D, W, false, U>(a, bt, hk, j0, jmax, k_lds, v_lds, none);
     __syncthreads();
     f32x4 s[NT][G_::MT], dp[NT][G_::MT];
 #pragma unroll
@@ -579,7 +579,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a_in, const BwdPlan& pl, hipStream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.f.ncb > 0) {
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, NT>), dim3(a.f.ncb, pl.hk, pl.batch), dim3(64 * W), 0, stream, a);
+      // scalar block ids per 16 rows when the block size allows (as the forward's tile loader)
+      const AttnArgs& f = a.f;
+      const int64_t span = (static_cast<int64_t>(f.bs) - 1) * std::max(f.kss, f.vss) * T::KVB + D * T::KVB;
+      const bool uni = f.bs % 16 == 0 && f.kss >= 0 && f.vss >= 0 && span < (int64_t{1} << 31);
+      const dim3 grid(a.f.ncb, pl.hk, pl.batch);
+      if (uni)
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, NT, true>), grid, dim3(64 * W), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, NT, false>), grid, dim3(64 * W), 0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
