@@ -32,6 +32,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define PKV_LDS __attribute__((address_space(3)))
+#ifndef PKV_V_AHEAD
+#define PKV_V_AHEAD 1
+#endif
 #ifndef PKV_MFMA_PRIO
 #define PKV_MFMA_PRIO 1
 #endif
@@ -427,6 +430,22 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
   if constexpr (T::EB == 2) {
 #if PKV_MFMA_PRIO
     __builtin_amdgcn_s_setprio(1);
+#endif
+#if PKV_V_AHEAD
+    if constexpr (kPinVReads) {
+      // one V operand read ahead of the MFMAs that use the current one
+      constexpr int KS = KT / 32;
+      u32x4 vnext = v_operand_bf16(v_lds, G_::VPITCH, 0, 0);
+#pragma unroll
+      for (int step = 0; step < G_::DT * KS; ++step) {
+        const int dt = step / KS, ks = step % KS;
+        const u32x4 va = vnext;
+        if (step + 1 < G_::DT * KS) vnext = v_operand_bf16(v_lds, G_::VPITCH, (step + 1) % KS, (step + 1) / KS);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st.o[nt][dt] = mfma_bf16(va, pb[nt][ks], st.o[nt][dt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else
 #endif
 #pragma unroll
     for (int dt = 0; dt < G_::DT; ++dt) {
