@@ -368,12 +368,14 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
   for (int nt = 0; nt < NT; ++nt) {
     const bool whole = kShortcuts && __all(j0 + KT <= lim[nt]);
     if (!whole) {
+      // key j0 + 16mt + 4G + i is past the limit iff 16mt + i >= lim - j0 - 4G
+      // (one bound per lane; the offsets are compile-time constants)
+      const int bound = lim[nt] - j0 - 4 * G;
 #pragma unroll
       for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = j0 + 16 * mt + 4 * G + i;
-          if (key >= lim[nt]) s[nt][mt][i] = -INFINITY;
+          if (16 * mt + i >= bound) s[nt][mt][i] = -INFINITY;
         }
     }
     float tmax = -INFINITY;
