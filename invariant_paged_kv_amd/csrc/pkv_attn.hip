@@ -52,12 +52,26 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #ifndef PKV_FULL_PREFETCH
 #define PKV_FULL_PREFETCH 1
 #endif
+#ifndef PKV_FULL_DB
+#define PKV_FULL_DB 1
+#endif
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND, bool U>
 __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   constexpr int COLS = W * NT * 16;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[G_::BYTES];
+  // bf16/FP8 with 4 waves: the next tile's loads are issued between the
+  // softmax and the P.V products of the current one (into registers the
+  // scores have freed).  With PKV_FULL_DB the K/V tile is double-buffered in
+  // LDS: at the start of tile t the staged tile t+1 is written into the buffer
+  // tile t-1 used, so one barrier per tile both publishes tile t and frees
+  // that buffer (two work groups per CU still fit).  fp32 and the
+  // fused-append variant (whose store of the new rows would spill) load each
+  // tile when it starts.  Past the item's last tile the rows clamp to
+  // jmax - 1, so the extra loads stay in bounds.
+  constexpr bool kPrefetch = PKV_FULL_PREFETCH && T::EB == 2 && W == 4 && !APPEND;
+  constexpr bool kDouble = kPrefetch && PKV_FULL_DB;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[(kDouble ? 2 : 1) * G_::BYTES];
   unsigned char* k_lds = lds;
   unsigned char* v_lds = lds + G_::KBYTES;
 
@@ -137,26 +151,33 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   }
 
   const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
-  // bf16/FP8 with 4 waves: the next tile's loads are issued between the
-  // softmax and the P.V products of the current one (into registers the
-  // scores have freed) and written to LDS after the next barrier; fp32 and
-  // the fused-append variant (whose store of the new rows would spill) load
-  // each tile when it starts.  Past the item's last tile the rows clamp to
-  // jmax - 1, so the extra issue stays in bounds.
-  constexpr bool kPrefetch = PKV_FULL_PREFETCH && T::EB == 2 && W == 4 && !APPEND;
   TileStage<T, D, W> stg;
   if constexpr (kPrefetch) tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC, jmax, stg, ap);
+  if constexpr (kDouble) {
+    // first tile into buffer 0, the second one's loads in flight
+    tile_commit<T, D, W, APPEND>(a, bt, hk, c_begin * KC, jmax, stg, k_lds, v_lds, ap);
+    tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC + KT, jmax, stg, ap);
+  }
   ChunkState<D, NT> st;
   for (int c = c_begin; c < c_end; ++c) {
     chunk_reset(st);
     const int jend = min((c + 1) * KC, jmax);
     for (int j0 = c * KC; j0 < jend; j0 += KT) {
       __syncthreads();
-      if constexpr (kPrefetch)
-        tile_commit<T, D, W, APPEND>(a, bt, hk, j0, jmax, stg, k_lds, v_lds, ap);
-      else
-        load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
-      __syncthreads();
+      if constexpr (kDouble) {
+        // tile j0 is in buffer (j0 / KT) & 1; the other one is free: stage tile j0 + KT there
+        const int cur = (j0 / KT) & 1;
+        unsigned char* const nk = lds + (cur ^ 1) * G_::BYTES;
+        tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, stg, nk, nk + G_::KBYTES, ap);
+        k_lds = lds + cur * G_::BYTES;
+        v_lds = k_lds + G_::KBYTES;
+      } else {
+        if constexpr (kPrefetch)
+          tile_commit<T, D, W, APPEND>(a, bt, hk, j0, jmax, stg, k_lds, v_lds, ap);
+        else
+          load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
+        __syncthreads();
+      }
       f32x4 s[NT][KT / 16];
       if constexpr (NT == 1) {
         qk_tile_lds<T, D>(k_lds, q[0], s[0]);  // one M tile of K operands live at a time
@@ -171,8 +192,10 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
 #endif
       }
       if constexpr (kPrefetch) {
-        softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(
-            st, s, lim, j0, a.mul, v_lds, [&] { tile_issue<T, D, W, APPEND, U>(a, bt, hk, j0 + KT, jmax, stg, ap); });
+        const int jn = kDouble ? j0 + 2 * KT : j0 + KT;
+        // V operands two P.V steps ahead where registers allow (scalar block ids)
+        softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0, true, U ? 2 : 1>(
+            st, s, lim, j0, a.mul, v_lds, [&] { tile_issue<T, D, W, APPEND, U>(a, bt, hk, jn, jmax, stg, ap); });
       } else {
         softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
       }

@@ -324,6 +324,29 @@ __device__ __forceinline__ u32x4 v_operand_bf16(const unsigned char* v_lds, int 
 #endif
 }
 
+// Butterfly steps across lanes 16 and 32 apart without an LDS round trip:
+// v_permlane16_swap / v_permlane32_swap with both operands x give, in every
+// lane, the pair (value of the lower lane, value of the upper lane) of its
+// xor partner pair, so both lanes of a pair combine the same two values in the
+// same operand order (max and add are commutative, so the bits equal those of
+// a shuffle-based butterfly).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // One tile of the chunk core for NT column groups.
 //   s        raw QK^T accumulators per column group (from qk_tile), consumed
@@ -354,16 +377,14 @@ struct NoMid {
 
 // `mid` runs between the softmax and the P.V products (the full-path kernels
 // issue the next tile's loads there, into registers the scores no longer use).
-template <class T, int D, int NT, bool kPinVReads = false, bool kShortcuts = true, class Mid = NoMid>
-__device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
-                                                const int (&lim)[NT], int j0, float mul,
-                                                const unsigned char* v_lds, const Mid& mid = Mid{}) {
+// The softmax half of the chunk core: masks, max, alpha, p, l, o *= alpha and,
+// for the bf16 compute type, the bf16 P operands pb (fp32 keeps p in s).
+template <class T, int D, int NT, bool kShortcuts = true>
+__device__ __forceinline__ void softmax_part(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
+                                             const int (&lim)[NT], int j0, float mul, u32x4 (&pb)[NT][KT / 32]) {
   using G_ = TileGeom<T, D>;
   const int lane = lane_id();
   const int G = lane >> 4;
-
-  // P operands: bf16 -> 2 PV steps of 32 keys (packed u32x4); fp32 -> s itself.
-  u32x4 pb[NT][KT / 32];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const bool whole = kShortcuts && __all(j0 + KT <= lim[nt]);
@@ -383,8 +404,8 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
     for (int mt = 0; mt < G_::MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[nt][mt][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_xor16(tmax);
+    tmax = max_xor32(tmax);
     // mul > 0, so the max of the scaled scores is the scaled max (rounding is monotone).
     const float m_tile = tmax * mul;
     const float m_old = st.m[nt];
@@ -427,22 +448,34 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
       }
     }
   }
+}
 
-  mid();
-  if constexpr (T::EB == 2) {
+// The P.V half of the chunk core for the bf16 compute type: o += P V by MFMA
+// in PV-step order.
+// kAhead: V operand reads in flight ahead of the MFMAs (with kPinVReads).
+template <class T, int D, int NT, bool kPinVReads = false, int kAhead = 1>
+__device__ __forceinline__ void pv_part(ChunkState<D, NT>& st, const u32x4 (&pb)[NT][KT / 32],
+                                        const unsigned char* v_lds) {
+  using G_ = TileGeom<T, D>;
+  static_assert(T::EB == 2, "bf16 compute type");
+  {
 #if PKV_MFMA_PRIO
     __builtin_amdgcn_s_setprio(1);
 #endif
 #if PKV_V_AHEAD
     if constexpr (kPinVReads) {
-      // one V operand read ahead of the MFMAs that use the current one
+      // V operands read kAhead steps ahead of the MFMAs that use them
       constexpr int KS = KT / 32;
-      u32x4 vnext = v_operand_bf16(v_lds, G_::VPITCH, 0, 0);
+      constexpr int NS = G_::DT * KS;
+      u32x4 vq[kAhead];
 #pragma unroll
-      for (int step = 0; step < G_::DT * KS; ++step) {
+      for (int i = 0; i < kAhead; ++i) vq[i] = v_operand_bf16(v_lds, G_::VPITCH, i % KS, i / KS);
+#pragma unroll
+      for (int step = 0; step < NS; ++step) {
         const int dt = step / KS, ks = step % KS;
-        const u32x4 va = vnext;
-        if (step + 1 < G_::DT * KS) vnext = v_operand_bf16(v_lds, G_::VPITCH, (step + 1) % KS, (step + 1) / KS);
+        const u32x4 va = vq[step % kAhead];
+        if (step + kAhead < NS)
+          vq[step % kAhead] = v_operand_bf16(v_lds, G_::VPITCH, (step + kAhead) % KS, (step + kAhead) / KS);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) st.o[nt][dt] = mfma_bf16(va, pb[nt][ks], st.o[nt][dt]);
         __builtin_amdgcn_sched_barrier(0);
@@ -465,6 +498,23 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
 #if PKV_MFMA_PRIO
     __builtin_amdgcn_s_setprio(0);
 #endif
+  }
+}
+
+template <class T, int D, int NT, bool kPinVReads = false, bool kShortcuts = true, int kAhead = 1,
+          class Mid = NoMid>
+__device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s)[NT][KT / 16],
+                                                const int (&lim)[NT], int j0, float mul,
+                                                const unsigned char* v_lds, const Mid& mid = Mid{}) {
+  using G_ = TileGeom<T, D>;
+  const int lane = lane_id();
+  const int G = lane >> 4;
+  // P operands: bf16 -> 2 PV steps of 32 keys (packed u32x4); fp32 -> s itself.
+  u32x4 pb[NT][KT / 32];
+  softmax_part<T, D, NT, kShortcuts>(st, s, lim, j0, mul, pb);
+  mid();
+  if constexpr (T::EB == 2) {
+    pv_part<T, D, NT, kPinVReads, kAhead>(st, pb, v_lds);
   } else {
     // fp32 PV step (mt, i): slot G <-> key 16mt + 4G + i.
     const unsigned char* col = v_lds + 4 * (lane & 15);
@@ -484,8 +534,8 @@ __device__ __forceinline__ void softmax_pv_tile(ChunkState<D, NT>& st, f32x4 (&s
 // Column sum of the per-lane partial l (lanes 16 apart hold the same column):
 // a fixed xor butterfly, so every lane of the column gets the same bits.
 __device__ __forceinline__ float column_sum(float x) {
-  x = x + __shfl_xor(x, 16);
-  x = x + __shfl_xor(x, 32);
+  x = add_xor16(x);
+  x = add_xor32(x);
   return x;
 }
 
