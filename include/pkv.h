@@ -142,7 +142,9 @@ typedef struct pkv_layout {
  * Buffers must stay alive until the stream passes this call.  Device data
  * preconditions (not checked): block ids in [0, num_blocks); seqlens_k[b] <=
  * min(max_seqlen_k, max_blocks_per_seq * block_size); row counts <=
- * max_seqlen_q; cache values at visible positions finite.  The split (decode)
+ * max_seqlen_q; cache values at visible positions finite.  A row with no
+ * visible key (e.g. seqlens_k[b] = 0, or a causal row at position < 0 when
+ * seqlens_k[b] is below the row count) gets out = 0 and lse = -inf.  The split (decode)
  * path needs a workspace; this entry point takes it from the stream-ordered
  * allocator (hipMallocAsync / hipFreeAsync on `stream`).
  * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (also softmax_scale <= 0 or not finite),

@@ -151,79 +151,83 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   }
 
   const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
-  TileStage<T, D, W> stg;
-  if constexpr (kPrefetch) tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC, jmax, stg, ap);
-  if constexpr (kDouble) {
-    // first tile into buffer 0, the second one's loads in flight
-    tile_commit<T, D, W, APPEND>(a, bt, hk, c_begin * KC, jmax, stg, k_lds, v_lds, ap);
-    tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC + KT, jmax, stg, ap);
-  }
-  ChunkState<D, NT> st;
-  for (int c = c_begin; c < c_end; ++c) {
-    chunk_reset(st);
-    const int jend = min((c + 1) * KC, jmax);
-    for (int j0 = c * KC; j0 < jend; j0 += KT) {
-      __syncthreads();
-      if constexpr (kDouble) {
-        // tile j0 is in buffer (j0 / KT) & 1; the other one is free: stage tile j0 + KT there
-        const int cur = (j0 / KT) & 1;
-        unsigned char* const nk = lds + (cur ^ 1) * G_::BYTES;
-        tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, stg, nk, nk + G_::KBYTES, ap);
-        k_lds = lds + cur * G_::BYTES;
-        v_lds = k_lds + G_::KBYTES;
-      } else {
-        if constexpr (kPrefetch)
-          tile_commit<T, D, W, APPEND>(a, bt, hk, j0, jmax, stg, k_lds, v_lds, ap);
-        else
-          load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
-        __syncthreads();
-      }
-      f32x4 s[NT][KT / 16];
-      if constexpr (NT == 1) {
-        qk_tile_lds<T, D>(k_lds, q[0], s[0]);  // one M tile of K operands live at a time
-      } else {
-#if PKV_QK_PER_MT
-        qk_tiles_lds<T, D, NT>(k_lds, q, s);   // one M tile of K operands, all column groups
-#else
-        KOps<T, D> kop;
-        k_operands_lds<T, D>(k_lds, kop);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
-#endif
-      }
-      if constexpr (kPrefetch) {
-        const int jn = kDouble ? j0 + 2 * KT : j0 + KT;
-        // V operands two P.V steps ahead where registers allow (scalar block ids)
-        softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0, true, U ? 2 : 1>(
-            st, s, lim, j0, a.mul, v_lds, [&] { tile_issue<T, D, W, APPEND, U>(a, bt, hk, jn, jmax, stg, ap); });
-      } else {
-        softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
-      }
+  // No visible key (only when seqlens_k is below the sequence's row count):
+  // nothing is loaded and the columns get out = 0, lse = -inf.
+  if (c_begin < c_end) {
+    TileStage<T, D, W> stg;
+    if constexpr (kPrefetch) tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC, jmax, stg, ap);
+    if constexpr (kDouble) {
+      // first tile into buffer 0, the second one's loads in flight
+      tile_commit<T, D, W, APPEND>(a, bt, hk, c_begin * KC, jmax, stg, k_lds, v_lds, ap);
+      tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC + KT, jmax, stg, ap);
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float lc = column_sum(st.l[nt]);
-      if constexpr (SPLIT) {
-        const int col = cols[nt];
-        if (col < ncols) {
-          const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.ps_row + c * a.ps_chunk;
-          if (G == 0) {
-            a.part_ml[2 * idx] = st.m[nt];
-            a.part_ml[2 * idx + 1] = lc;
-          }
-          float* po = a.part_o + idx * D;
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * G) = st.o[nt][dt];
+    ChunkState<D, NT> st;
+    for (int c = c_begin; c < c_end; ++c) {
+      chunk_reset(st);
+      const int jend = min((c + 1) * KC, jmax);
+      for (int j0 = c * KC; j0 < jend; j0 += KT) {
+        __syncthreads();
+        if constexpr (kDouble) {
+          // tile j0 is in buffer (j0 / KT) & 1; the other one is free: stage tile j0 + KT there
+          const int cur = (j0 / KT) & 1;
+          unsigned char* const nk = lds + (cur ^ 1) * G_::BYTES;
+          tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, stg, nk, nk + G_::KBYTES, ap);
+          k_lds = lds + cur * G_::BYTES;
+          v_lds = k_lds + G_::KBYTES;
+        } else {
+          if constexpr (kPrefetch)
+            tile_commit<T, D, W, APPEND>(a, bt, hk, j0, jmax, stg, k_lds, v_lds, ap);
+          else
+            load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
+          __syncthreads();
         }
-      } else {
-        if (st.m[nt] != -INFINITY) {
-          const FoldCoef<T> f = fold_coef<T>(M[nt], st.m[nt]);
-          Ls[nt] = fold_val(Ls[nt], f.a, lc, f.b);
+        f32x4 s[NT][KT / 16];
+        if constexpr (NT == 1) {
+          qk_tile_lds<T, D>(k_lds, q[0], s[0]);  // one M tile of K operands live at a time
+        } else {
+#if PKV_QK_PER_MT
+          qk_tiles_lds<T, D, NT>(k_lds, q, s);   // one M tile of K operands, all column groups
+#else
+          KOps<T, D> kop;
+          k_operands_lds<T, D>(k_lds, kop);
 #pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt)
+          for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
+#endif
+        }
+        if constexpr (kPrefetch) {
+          const int jn = kDouble ? j0 + 2 * KT : j0 + KT;
+          // V operands two P.V steps ahead where registers allow (scalar block ids)
+          softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0, true, U ? 2 : 1>(
+              st, s, lim, j0, a.mul, v_lds, [&] { tile_issue<T, D, W, APPEND, U>(a, bt, hk, jn, jmax, stg, ap); });
+        } else {
+          softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
+        }
+      }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) O[nt][dt][i] = fold_val(O[nt][dt][i], f.a, st.o[nt][dt][i], f.b);
-          M[nt] = f.mn;
+      for (int nt = 0; nt < NT; ++nt) {
+        const float lc = column_sum(st.l[nt]);
+        if constexpr (SPLIT) {
+          const int col = cols[nt];
+          if (col < ncols) {
+            const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.ps_row + c * a.ps_chunk;
+            if (G == 0) {
+              a.part_ml[2 * idx] = st.m[nt];
+              a.part_ml[2 * idx + 1] = lc;
+            }
+            float* po = a.part_o + idx * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * G) = st.o[nt][dt];
+          }
+        } else {
+          if (st.m[nt] != -INFINITY) {
+            const FoldCoef<T> f = fold_coef<T>(M[nt], st.m[nt]);
+            Ls[nt] = fold_val(Ls[nt], f.a, lc, f.b);
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) O[nt][dt][i] = fold_val(O[nt][dt][i], f.a, st.o[nt][dt][i], f.b);
+            M[nt] = f.mn;
+          }
         }
       }
     }

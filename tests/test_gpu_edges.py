@@ -101,6 +101,14 @@ def test_degenerate_batches():
     assert torch.all(lse[r[2]:r[2] + 1] == -math.inf)      # n = 1, L = 2: first row at position -1
     for path in (1, 2):
         gc.assert_bitwise(gc.run(case, path=path), (out, lse), f"path {path}")
+    # the first sequence has rows but no keys: no path may read its block-table row
+    # (a read before the table) -- its rows see nothing, the other sequence is normal
+    first = gc.make_case(4310, "bf16", 2, 8, 2, 128, 16, 700, "contiguous", True, [4, 2], seqlens=[0, 700])
+    fo, fl = gc.run(first)
+    gc.check_oracle(first, fo, fl)
+    assert torch.all(fl[0:4] == -math.inf) and torch.all(fo[0:4] == 0)
+    for path in (1, 2):
+        gc.assert_bitwise(gc.run(first, path=path), (fo, fl), f"first empty, path {path}")
     # a zero-row call is a no-op
     empty = torch.empty((0, 8, 128), dtype=torch.bfloat16, device=gc.DEV)
     o, l = pkv.attn_forward(empty, case.pool.k, case.pool.v, case.block_table, case.seqlens_d(),
