@@ -1,13 +1,20 @@
 // pkv_attn.hip -- attention kernels of libpkv for gfx950.
 //
-//   attn_kernel<SPLIT=true>   decode path: one work item per (sequence, KV head,
-//                             column block, run of chunks); writes one fp32
-//                             partial (max, sum, o[d]) per chunk and column.
-//   merge_kernel              decode path: folds a row's chunk partials in
-//                             ascending chunk index, then the final write.
-//   attn_kernel<SPLIT=false>  prefill path: one work item per (sequence, KV head,
-//                             column block); runs the chunks in ascending order
-//                             and folds them in registers, then the final write.
+// Split (decode) path: one work item per (sequence, KV head, column block, run
+// of chunks) writes one fp32 partial (max, sum, o[d]) per chunk and column;
+// merge_kernel then folds a row's partials in ascending chunk index and makes
+// the final write.
+//   decode_kernel             bf16, up to 16 columns per KV head: one wave, K/V
+//                             loaded straight into registers a tile ahead.
+//   decode2_kernel            FP8 caches: the same with two tiles in flight.
+//   attn_kernel<SPLIT=true>   more columns (or fp32): 4 waves sharing LDS tiles.
+// Full (prefill) path: one work item per (sequence, KV head, column block)
+// runs the chunks in ascending order, folds them in registers and makes the
+// final write.
+//   attn_kernel<SPLIT=false>  4 waves x 2 column groups, LDS tiles double-buffered
+//                             from a register stage.
+//   prefill_kernel            the 8-wave x 16-column pipelined variant (kept as a
+//                             bitwise cross-check, PKV_OPT_FULL_KERNEL = 1).
 //
 // A "column" is one (query row, query head) pair of a sequence; the g = Hq/Hkv
 // query heads of a KV head share every K/V tile a work item stages in LDS, so
