@@ -85,16 +85,17 @@ enum pkv_status {
 /*
  * Shapes and strides of one call.  All strides are in elements.
  *   dtype               pkv_dtype (element types of q/out and of the cache/new K/V)
- *   batch               B, number of sequences
+ *   batch               B, number of sequences, <= 65535 (a launch-grid dimension)
  *   num_heads_q         Hq; num_heads_q % num_heads_k == 0
- *   num_heads_k         Hkv
+ *   num_heads_k         Hkv, <= 65535
  *   head_dim            d, 64 or 128
  *   block_size          tokens per cache block, >= 1
  *   max_blocks_per_seq  row length of block_table ([batch, max_blocks_per_seq], int32)
  *   max_seqlen_q        host-side bound on every cu_seqlens_q[b+1] - cu_seqlens_q[b]
  *   max_seqlen_k        host-side bound on every seqlens_k[b]; 0 means
  *                       max_blocks_per_seq * block_size
- *   total_q             rows of q / out / lse (cu_seqlens_q[batch])
+ *   total_q             rows of q / out / lse (cu_seqlens_q[batch]);
+ *                       total_q * num_heads_q <= 2^31 - 1
  *   num_blocks          blocks in the pool (used only by debug checks)
  *   k_* / v_*_stride    element strides of the K and V caches: block, slot, head
  *   k_scale, v_scale    K = stored * k_scale, V = stored * v_scale (0 means 1; must be

@@ -70,6 +70,12 @@ int validate(const pkv_layout* l) {
   if (l->batch < 0) return fail(PKV_ERR_SHAPE, "batch %d < 0", l->batch);
   if (l->num_heads_k < 1 || l->num_heads_q < 1 || l->num_heads_q % l->num_heads_k != 0)
     return fail(PKV_ERR_SHAPE, "num_heads_q %d must be a positive multiple of num_heads_k %d", l->num_heads_q, l->num_heads_k);
+  // launch-grid limits: sequences and KV heads are grid dimensions of at most
+  // 65535, and (row, query head) pairs are counted in 31 bits
+  if (l->batch > 65535 || l->num_heads_k > 65535)
+    return fail(PKV_ERR_SHAPE, "batch %d and num_heads_k %d must be at most 65535", l->batch, l->num_heads_k);
+  if (l->total_q > 0 && static_cast<int64_t>(l->total_q) * l->num_heads_q > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "total_q * num_heads_q exceeds 2^31 - 1");
   if (l->head_dim != 64 && l->head_dim != 128) return fail(PKV_ERR_SHAPE, "head_dim %d is not 64 or 128", l->head_dim);
   if (l->block_size < 1) return fail(PKV_ERR_SHAPE, "block_size %d < 1", l->block_size);
   if (l->max_blocks_per_seq < 0) return fail(PKV_ERR_SHAPE, "max_blocks_per_seq %d < 0", l->max_blocks_per_seq);
@@ -96,6 +102,7 @@ struct Plan {
   int cpi;
   size_t ws_bytes;
   size_t off_ml;
+  bool grid_ok;  // work items along the first grid dimension fit in 31 bits
 };
 
 size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
@@ -136,6 +143,7 @@ Plan make_plan(const pkv_layout& l) {
   p.lp.full = full;
   p.lp.waves = waves;
   p.lp.items = std::max(1, (p.maxc + p.cpi - 1) / p.cpi);
+  p.grid_ok = static_cast<int64_t>(p.ncb) * (full ? 1 : p.lp.items) <= INT32_MAX;
   p.lp.batch = l.batch;
   p.lp.hk = l.num_heads_k;
   p.lp.total_q = l.total_q;
@@ -177,6 +185,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   if (l->batch == 0 || l->total_q == 0) return ok();
   Plan p = make_plan(*l);
   p.lp.append = append;
+  if (!p.grid_ok) return fail(PKV_ERR_SHAPE, "too many column blocks x key splits for one launch");
   bool allocated = false;
   if (p.ws_bytes > 0) {
     if (own_ws) {
@@ -281,6 +290,8 @@ int run_partials(const void* q, const void* k_cache, const void* v_cache, const 
   a.mbps = l->max_blocks_per_seq;
   const int cpb = waves == 1 ? 16 : 16 * 4 * pkv::kSplitGroups;
   a.ncb = static_cast<int>(std::max<int64_t>(1, (cols + cpb - 1) / cpb));
+  if (static_cast<int64_t>(a.ncb) * lp.items > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "too many column blocks x key splits for one launch");
   a.maxc = max_chunks;
   a.cpi = static_cast<int>(cpi);
   a.chunk0 = c0;

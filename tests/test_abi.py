@@ -62,6 +62,11 @@ def good_layout(**over):
     ({"k_scale": -1.0}, -2),
     ({"v_scale": float("nan")}, -2),
     ({"k_scale": 0.5, "v_scale": 0.0}, 0),
+    ({"batch": 65535}, 0),                     # launch-grid limits
+    ({"batch": 65536}, -2),
+    ({"num_heads_q": 65536 * 2, "num_heads_k": 65536}, -2),
+    ({"total_q": ((1 << 31) - 1) // 16}, 0),
+    ({"total_q": ((1 << 31) - 1) // 16 + 1}, -2),   # total_q * num_heads_q past 2^31 - 1
 ])
 def test_validate_layout(over, code):
     L = pkv.lib()
