@@ -107,7 +107,7 @@ struct Plan {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
 
-Plan make_plan(const pkv_layout& l) {
+Plan make_plan(const pkv_layout& l, bool append = false) {
   Plan p{};
   const int g = l.num_heads_q / l.num_heads_k;
   const int64_t cols = static_cast<int64_t>(l.max_seqlen_q) * g;
@@ -132,10 +132,22 @@ Plan make_plan(const pkv_layout& l) {
   // the pipelined 8-wave x 16-column kernel is asked for; both give the same
   // bits.  Measured on the 8 x 8192 prefill 609-618 against 441 TFLOP/s, and
   // on 64 rows x 131072 keys 560-565 against 366.
-  bool full4 = false;
-  if (full && l.dtype != PKV_F32) full4 = g_opt_full_kernel.load() != 1;
+  // bf16/FP8 full path: 8 waves x 32 columns (one work group per CU, 256
+  // columns sharing each K/V tile stream) when a (sequence, KV head) has few
+  // columns over a long context -- the re-score of a generated sequence, where
+  // every column block streams the whole cache: 64-256 rows x 32768-131072
+  // keys measured 5-9% faster, 1024 columns 2%; with more columns per KV head
+  // the 4-wave kernel's extra work groups balance better (2800-8192 columns:
+  // 1-11% slower with 8 waves, 32768: equal).  Both give the same bits.
+  bool full4 = false, full8 = false;
+  if (full && l.dtype != PKV_F32) {
+    const int64_t fk = g_opt_full_kernel.load();
+    full4 = fk != 1;
+    full8 = !append && (fk == 3 || (fk == 0 && cols <= 1024 && mk >= 16384));
+  }
   p.lp.full4 = full4;
-  const int cols_per_block = full ? 128 : (waves == 1 ? 16 : 16 * 4 * pkv::kSplitGroups);
+  p.lp.full8 = full8;
+  const int cols_per_block = full ? (full8 ? 256 : 128) : (waves == 1 ? 16 : 16 * 4 * pkv::kSplitGroups);
   p.ncb = static_cast<int>(std::max<int64_t>(1, (cols + cols_per_block - 1) / cols_per_block));
   int64_t cpi = g_opt_split_chunks.load();
   if (cpi <= 0) cpi = 1;
@@ -183,7 +195,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(PKV_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (l->batch == 0 || l->total_q == 0) return ok();
-  Plan p = make_plan(*l);
+  Plan p = make_plan(*l, append);
   p.lp.append = append;
   if (!p.grid_ok) return fail(PKV_ERR_SHAPE, "too many column blocks x key splits for one launch");
   bool allocated = false;
@@ -532,7 +544,7 @@ int pkv_set_option(int option, int64_t value) {
       g_opt_split_chunks.store(value);
       return ok();
     case PKV_OPT_FULL_KERNEL:
-      if (value < 0 || value > 2) return fail(PKV_ERR_OPTION, "PKV_OPT_FULL_KERNEL must be 0, 1 or 2");
+      if (value < 0 || value > 3) return fail(PKV_ERR_OPTION, "PKV_OPT_FULL_KERNEL must be in 0..3");
       g_opt_full_kernel.store(value);
       return ok();
     default:

@@ -64,7 +64,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #endif
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND, bool U>
-__global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   constexpr int COLS = W * NT * 16;
   // bf16/FP8 with 4 waves: the next tile's loads are issued between the
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_kernel(AttnArgs a) {
   // fused-append variant (whose store of the new rows would spill) load each
   // tile when it starts.  Past the item's last tile the rows clamp to
   // jmax - 1, so the extra loads stay in bounds.
-  constexpr bool kPrefetch = PKV_FULL_PREFETCH && T::EB == 2 && W == 4 && !APPEND;
+  constexpr bool kPrefetch = PKV_FULL_PREFETCH && T::EB == 2 && (W == 4 || W == 8) && !APPEND;
   constexpr bool kDouble = kPrefetch && PKV_FULL_DB;
   __shared__ __attribute__((aligned(16))) unsigned char lds[(kDouble ? 2 : 1) * G_::BYTES];
   unsigned char* k_lds = lds;
@@ -916,6 +916,15 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   const bool uni = a.bs % 16 == 0 && a.kss >= 0 && a.vss >= 0 && span < (int64_t{1} << 31);
   if (pl.full) {
     dim3 grid(a.ncb, pl.hk, pl.batch);
+    if constexpr (T::EB == 2 && !APPEND) {
+      if (pl.full8) {
+        if (uni)
+          hipLaunchKernelGGL((attn_kernel<T, D, 8, 2, false, APPEND, true>), grid, dim3(512), 0, stream, a);
+        else
+          hipLaunchKernelGGL((attn_kernel<T, D, 8, 2, false, APPEND, false>), grid, dim3(512), 0, stream, a);
+        return hipGetLastError();
+      }
+    }
     if (T::EB == 2 && !pl.full4) {
       if constexpr (T::EB == 2) hipLaunchKernelGGL((prefill_kernel<T, D, 8, APPEND>), grid, dim3(512), 0, stream, a);
     } else if (uni) {

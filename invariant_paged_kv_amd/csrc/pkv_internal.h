@@ -66,6 +66,7 @@ constexpr int kSplitGroups = PKV_SPLIT_NT;
 struct LaunchPlan {
   bool full;       // prefill kernel (true) or split kernels + merge (false)
   bool full4;      // full path, bf16/FP8: 4 waves x 32 columns (attn_kernel) instead of the 8-wave pipelined kernel
+  bool full8;      // full path, bf16/FP8, no fused append: 8 waves x 32 columns (attn_kernel), one work group per CU
   bool append;     // fused append of k_new / v_new
   bool skip_merge; // split path: write the chunk partials only
   int waves;       // split path: waves per work group (1 or 4)

@@ -3,8 +3,8 @@ block sizes give the same bits.
 
 The block size only decides where a key's row is stored (key j of a sequence
 sits in table entry j / block_size, slot j % block_size); it enters no
-arithmetic.  So for every path -- the split decode kernels, the 4-wave full
-kernel and the 4-wave split kernel -- out and lse must be bitwise identical
+arithmetic.  So for every path -- the split decode kernels, the 4-wave and
+8-wave full kernels and the 4-wave split kernel -- out and lse must be bitwise identical
 across block sizes.  The sizes cover both ways the kernels address a tile:
 multiples of 16 (one block id per 16-row group, read with a scalar load) and
 other sizes (a block id per row).  Slots the tables do not reference hold NaN,
@@ -79,24 +79,25 @@ def case_for(pool, table, q, lens, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("mode", ["decode", "prefill-full", "prefill-split"])
+@pytest.mark.parametrize("mode", ["decode", "prefill-full", "prefill-full8", "prefill-split"])
 def test_block_size_invariance(dtype, mode):
     announce(f"block-size invariance {dtype} {mode}")
     ks, vs, g = dense_kv(9500 + (dtype == "fp8"), dtype)
     lens = [1, 1, 1, 1] if mode == "decode" else [min(n, 150) for n in SEQLENS]
     qdt = "bf16" if dtype == "fp8" else dtype
     q = gen.randn((sum(lens), HQ, D), qdt, generator=g)
-    path = {"decode": None, "prefill-full": 2, "prefill-split": 1}[mode]
+    path = {"decode": None, "prefill-full": 2, "prefill-full8": 2, "prefill-split": 1}[mode]
+    fk = 3 if mode == "prefill-full8" else None
     ref = None
     for i, bs in enumerate(BLOCK_SIZES):
         layout = "interleaved" if i % 2 == 0 else "contiguous"
         pool, table = paged(ks, vs, bs, dtype, layout, seed=9600 + bs)
         case = case_for(pool, table, q, lens, dtype)
-        got = gc.run(case, path=path)
+        got = gc.run(case, path=path, full_kernel=fk)
         assert not torch.isnan(got[0].float()).any(), f"NaN in out at block size {bs}"
         if ref is None:
             ref = got
-            if mode != "prefill-split":
+            if mode not in ("prefill-split", "prefill-full8"):
                 # anchor the shared result to the oracle (bf16 tolerances; FP8 queries are bf16)
                 gc.check_oracle(case, *got)
         else:

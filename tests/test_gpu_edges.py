@@ -46,6 +46,8 @@ def test_odd_block_sizes(bs, layout):
     gc.assert_bitwise(gc.run(case, pool=other), (out, lse), "layouts")
     for path in (1, 2):
         gc.assert_bitwise(gc.run(case, path=path), (out, lse), f"path {path}")
+    for fk in (1, 3):   # the other full-path kernels (per-row block ids when bs % 16 != 0)
+        gc.assert_bitwise(gc.run(case, path=2, full_kernel=fk), (out, lse), f"full kernel {fk}")
 
 
 @pytest.mark.parametrize("bs", [1, 7, 100])

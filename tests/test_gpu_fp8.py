@@ -111,7 +111,7 @@ def test_fp8_parity_and_paths(spec):
     for path in (1, 2):
         for split in (None, 1, 3):
             gc.assert_bitwise(run(case, path=path, split=split), ref, f"path {path} split {split}")
-    for fk in (1, 2):
+    for fk in (1, 2, 3):
         gc.assert_bitwise(run(case, path=2, full_kernel=fk), ref, f"full kernel {fk}")
     other = gc.to_device(gen.relayout(gc.host_pool(case.pool), "contiguous" if layout == "interleaved" else "interleaved"))
     gc.assert_bitwise(run(case, pool=other), ref, "layout")

@@ -52,7 +52,7 @@ def test_split_count_and_path_invariance(dtype, d):
     for path in (1, 2):
         for split in (1, 2, 3, 7, 64):
             gc.assert_bitwise(gc.run(case, path=path, split_chunks=split), ref, f"path {path} split {split}")
-    for fk in (1, 2):
+    for fk in (1, 2, 3):
         gc.assert_bitwise(gc.run(case, path=2, full_kernel=fk), ref, f"full path, kernel {fk}")
 
 
@@ -92,7 +92,7 @@ def test_unread_memory_is_never_read():
     gc.assert_bitwise(gc.run(case, block_table=bt2), ref, "poisoned pool and table tail")
     for path in (1, 2):
         gc.assert_bitwise(gc.run(case, block_table=bt2, path=path), ref, f"poisoned, path {path}")
-    for fk in (1, 2):
+    for fk in (1, 2, 3):
         gc.assert_bitwise(gc.run(case, block_table=bt2, path=2, full_kernel=fk), ref, f"poisoned, full kernel {fk}")
 
 
