@@ -57,15 +57,25 @@ def run(case: Case, pool: Optional[gen.PagedKV] = None, block_table=None, q=None
     q = case.q if q is None else q
     sl = case.seqlens if seqlens is None else seqlens
     cul = case.cu if cu is None else cu
+    # NaN-filled outputs: an element a kernel does not write cannot pass as the
+    # stale copy of an earlier run's result
+    out0 = torch.full_like(q, float("nan"))
+    lse0 = torch.full((q.shape[0], q.shape[1]), float("nan"), dtype=torch.float32, device=q.device)
     with pkv.options(path=path, split_chunks=split_chunks, full_kernel=full_kernel):
         out, lse = pkv.attn_forward(
             q, pool.k, pool.v, bt, torch.tensor(sl, dtype=torch.int32, device=DEV),
             torch.tensor(cul, dtype=torch.int32, device=DEV),
             case.causal if causal is None else causal, case.scale if scale is None else scale,
             max_seqlen_q=max(cul[i + 1] - cul[i] for i in range(len(cul) - 1)),
-            max_seqlen_k=max(sl))
+            max_seqlen_k=max(sl), out=out0, lse=lse0)
     torch.cuda.synchronize()
     return out, lse
+
+
+def nan_outputs(q: torch.Tensor) -> dict:
+    """out / lse buffers for q, filled with NaN (every element must be written)."""
+    return dict(out=torch.full_like(q, float("nan")),
+                lse=torch.full((q.shape[0], q.shape[1]), float("nan"), dtype=torch.float32, device=q.device))
 
 
 def bits(t: torch.Tensor) -> torch.Tensor:

@@ -59,7 +59,9 @@ def test_gpu_golden(name):
     out, lse = pkv.attn_forward(q.to(gc.DEV), dp.k, dp.v, bt.to(gc.DEV),
                                 torch.tensor(seqlens, dtype=torch.int32, device=gc.DEV),
                                 torch.tensor(cu, dtype=torch.int32, device=gc.DEV), causal, 1.0 / math.sqrt(d),
-                                max_seqlen_q=max(lens), max_seqlen_k=max(seqlens))
+                                max_seqlen_q=max(lens), max_seqlen_k=max(seqlens),
+                                out=torch.full_like(q.to(gc.DEV), float("nan")),
+                                lse=torch.full((cu[-1], hq), float("nan"), dtype=torch.float32, device=gc.DEV))
     torch.cuda.synchronize()
     tol_o, tol_l = (1e-5, 1e-6) if dtype == "f32" else (2e-2, 1e-3)
     want_l = np.array(rec["lse"], dtype=np.float64)

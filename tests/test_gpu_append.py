@@ -47,7 +47,8 @@ def unfused(q, kn, vn, pool, bt, seqlens, cu, causal, scale, max_q, max_k, path=
     cu_d = torch.tensor(cu, dtype=torch.int32, device=gc.DEV)
     pkv.cache_write(kn, vn, pool.k, pool.v, bt, sk - L, cu_d)
     with pkv.options(path=path):
-        return pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu_d, causal, scale, max_seqlen_q=max_q, max_seqlen_k=max_k)
+        return pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu_d, causal, scale, max_seqlen_q=max_q, max_seqlen_k=max_k,
+                                **gc.nan_outputs(q))
 
 
 def fused(q, kn, vn, pool, bt, seqlens, cu, causal, scale, max_q, max_k, path=None, split=None):

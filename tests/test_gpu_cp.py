@@ -63,7 +63,7 @@ def kw(case):
 def forward(case):
     out, lse = pkv.attn_forward(case.q, case.pool.k, case.pool.v, case.block_table, case.seqlens_d(), case.cu_d(),
                                 case.causal, case.scale, k_scale=case.extra["k_scale"],
-                                v_scale=case.extra["v_scale"], **kw(case))
+                                v_scale=case.extra["v_scale"], **kw(case), **gc.nan_outputs(case.q))
     torch.cuda.synchronize()
     return out, lse
 
@@ -85,7 +85,7 @@ def shares(case, bounds, max_chunks):
 def merge(case, po, pm):
     out, lse = pkv.attn_merge_partials(po, pm, case.q, case.pool.k, case.pool.v, case.block_table,
                                        case.seqlens_d(), case.cu_d(), case.causal,
-                                       v_scale=case.extra["v_scale"], **kw(case))
+                                       v_scale=case.extra["v_scale"], **kw(case), **gc.nan_outputs(case.q))
     torch.cuda.synchronize()
     return out, lse
 

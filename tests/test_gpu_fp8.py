@@ -62,12 +62,14 @@ def run(case, pool=None, block_table=None, q=None, seqlens=None, cu=None, path=N
     q = case.q if q is None else q
     sl = case.seqlens if seqlens is None else seqlens
     cul = case.cu if cu is None else cu
+    out0 = torch.full_like(q, float("nan"))   # unwritten elements stay NaN
+    lse0 = torch.full((q.shape[0], q.shape[1]), float("nan"), dtype=torch.float32, device=q.device)
     with pkv.options(path=path, split_chunks=split, full_kernel=full_kernel):
         out, lse = pkv.attn_forward(
             q, pool.k, pool.v, bt, torch.tensor(sl, dtype=torch.int32, device=gc.DEV),
             torch.tensor(cul, dtype=torch.int32, device=gc.DEV), case.causal, case.scale,
             max_seqlen_q=max(cul[i + 1] - cul[i] for i in range(len(cul) - 1)), max_seqlen_k=max(sl),
-            k_scale=case.extra["k_scale"], v_scale=case.extra["v_scale"])
+            k_scale=case.extra["k_scale"], v_scale=case.extra["v_scale"], out=out0, lse=lse0)
     torch.cuda.synchronize()
     return out, lse
 
@@ -153,7 +155,7 @@ def test_fp8_generate_then_rescore_and_fused_append():
         sk_old = torch.full((batch,), n, dtype=torch.int32, device=gc.DEV)
         pkv.cache_write(kn[t].contiguous(), vn[t].contiguous(), pool.k, pool.v, bt, sk_old, cu1)
         o, l = pkv.attn_forward(q[t].contiguous(), pool.k, pool.v, bt, sk_old + 1, cu1, True, scale,
-                                max_seqlen_q=1, max_seqlen_k=n_final, k_scale=ks, v_scale=vs)
+                                max_seqlen_q=1, max_seqlen_k=n_final, k_scale=ks, v_scale=vs, **gc.nan_outputs(q[t]))
         of, lf = pkv.attn_forward_append(q[t].contiguous(), kn[t].contiguous(), vn[t].contiguous(), pool_f.k,
                                          pool_f.v, bt, sk_old + 1, cu1, True, scale, max_seqlen_q=1,
                                          max_seqlen_k=n_final, k_scale=ks, v_scale=vs)

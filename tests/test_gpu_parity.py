@@ -299,7 +299,7 @@ def c5_generate_rescore(batch: int, n_final: int, seed: int = 1005, steps: int =
         pos = torch.full((batch,), prefix + t, dtype=torch.int32, device=gc.DEV)
         pkv.cache_write(kn[t].contiguous(), vn[t].contiguous(), pool.k, pool.v, bt, pos, cu1)
         o, l = pkv.attn_forward(q[t].contiguous(), pool.k, pool.v, bt, pos + 1, cu1, True, scale,
-                                max_seqlen_q=1, max_seqlen_k=prefix + t + 1)
+                                max_seqlen_q=1, max_seqlen_k=prefix + t + 1, **gc.nan_outputs(q[t]))
         dec_out.append(o)
         dec_lse.append(l)
     torch.cuda.synchronize()
