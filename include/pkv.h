@@ -191,7 +191,11 @@ int pkv_attn_forward_append(const void* q, const void* k_new, const void* v_new,
                             const int32_t* cu_seqlens_q, int causal, float softmax_scale, void* out, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes the split path needs for this layout (0 if it is never used). */
+/* Workspace bytes the split path needs for this layout (0 if it is never used):
+ * the fp32 chunk partials (total_q * Hq * chunks * (d + 2) floats) and, when
+ * the one-wave bf16/FP8 decode kernels take a longest-first job list (at most
+ * 16 chunks of keys and more than 2048 (sequence, KV head, chunk) slots),
+ * 2 * (batch + 1) int32 prefix counts; each part rounded up to 256 bytes. */
 size_t pkv_attn_workspace_size(const pkv_layout* kv_strides);
 
 /*

@@ -254,6 +254,97 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
 }
 
 // ---------------------------------------------------------------------------
+// Longest-first job list of the one-wave decode kernels.  With one chunk per
+// work item the items of a ragged batch differ only in their last chunk, so
+// dispatching every full chunk first and the partial last chunks after them
+// keeps short items for the end of the grid instead of long ones.  A job is
+// identified by (sequence, KV head, chunk) exactly as in the grid mapping, so
+// the order changes no bit.
+//
+// decode_plan_kernel (one work group) writes the exclusive prefix counts, over
+// sequences in order, of full chunks F_b = n_b / KC and partial chunks
+// P_b = (n_b % KC != 0) of the sequences that have rows (with one column
+// block, the last row of a sequence sees all n_b keys).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* seqlens_k, const int32_t* cu_q, int batch,
+                                                           int32_t* pref) {
+  __shared__ int32_t sf[1024], sp[1024];
+  __shared__ int32_t carry[2];
+  const int t = threadIdx.x;
+  if (t == 0) carry[0] = carry[1] = 0;
+  __syncthreads();
+  for (int base = 0; base < batch; base += 1024) {
+    const int b = base + t;
+    int f = 0, p = 0;
+    if (b < batch) {
+      const int n = seqlens_k[b];
+      const int L = cu_q[b + 1] - cu_q[b];
+      if (L > 0 && n > 0) {
+        f = n / KC;
+        p = (n % KC) != 0;
+      }
+    }
+    sf[t] = f;
+    sp[t] = p;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
+      const int xf = t >= d ? sf[t - d] : 0;
+      const int xp = t >= d ? sp[t - d] : 0;
+      __syncthreads();
+      sf[t] += xf;
+      sp[t] += xp;
+      __syncthreads();
+    }
+    if (b < batch) {
+      pref[b] = carry[0] + sf[t] - f;
+      pref[batch + 1 + b] = carry[1] + sp[t] - p;
+    }
+    __syncthreads();
+    if (t == 0) {
+      carry[0] += sf[1023];
+      carry[1] += sp[1023];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    pref[batch] = carry[0];
+    pref[2 * batch + 1] = carry[1];
+  }
+}
+
+// The (sequence, KV head, chunk) of job x; false past the last job.
+__device__ __forceinline__ bool decode_job(const AttnArgs& a, int x, int& b, int& hk, int& c) {
+  using cint = const __attribute__((address_space(4))) int32_t;
+  cint* pf = (cint*)a.job_pref;
+  cint* pp = pf + a.nbatch + 1;
+  const int H = a.nhk;
+  const int nfull = pf[a.nbatch] * H;
+  int m = x;
+  cint* pr = pf;
+  if (m >= nfull) {
+    m -= nfull;
+    pr = pp;
+    if (m >= pp[a.nbatch] * H) return false;
+  }
+  int lo = 0, hi = a.nbatch;  // largest b with H * pr[b] <= m (pr[0] = 0, H * pr[batch] > m)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pr[mid] * H <= m) lo = mid; else hi = mid;
+  }
+  b = lo;
+  const int r = m - pr[b] * H;
+  if (pr == pf) {
+    const int f = pf[b + 1] - pf[b];  // this sequence's full chunks, per KV head
+    hk = r / f;
+    c = r - hk * f;
+  } else {
+    hk = r;
+    c = a.seqlens_k[b] / KC;
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
 // Decode split kernel: one wave per work item (sequence, KV head, 16 columns,
 // run of chunks), for up to 16 query columns per KV head (g * L <= 16).
 //
@@ -629,10 +720,14 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   // head): concurrently running waves then read different cache blocks
   // (ordering the KV heads of one chunk next to each other measured ~9%
   // slower on the long-context workload).
-  const int b = blockIdx.z;
-  const int hk = blockIdx.y;
-  const int cb = blockIdx.x % a.ncb;
-  const int item = blockIdx.x / a.ncb;
+  int b = blockIdx.z;
+  int hk = blockIdx.y;
+  int cb = blockIdx.x % a.ncb;
+  int item = blockIdx.x / a.ncb;
+  if (a.job_pref) {  // longest-first job list (one column block, one chunk per item)
+    cb = 0;
+    if (!decode_job(a, blockIdx.x, b, hk, item)) return;
+  }
   const int n = a.seqlens_k[b];
   const int q0 = a.cu_q[b];
   const int L = a.cu_q[b + 1] - q0;
@@ -770,10 +865,14 @@ __global__ __launch_bounds__(64, 2) void decode2_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
 
-  const int b = blockIdx.z;
-  const int hk = blockIdx.y;
-  const int cb = blockIdx.x % a.ncb;
-  const int item = blockIdx.x / a.ncb;
+  int b = blockIdx.z;
+  int hk = blockIdx.y;
+  int cb = blockIdx.x % a.ncb;
+  int item = blockIdx.x / a.ncb;
+  if (a.job_pref) {  // longest-first job list (one column block, one chunk per item)
+    cb = 0;
+    if (!decode_job(a, blockIdx.x, b, hk, item)) return;
+  }
   const int n = a.seqlens_k[b];
   const int q0 = a.cu_q[b];
   const int L = a.cu_q[b + 1] - q0;
@@ -935,6 +1034,14 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
     return hipGetLastError();
   }
   dim3 grid(a.ncb * pl.items, pl.hk, pl.batch);
+  if (pl.lpt) {
+    // prefix counts of the longest-first job list, then one work item per job slot
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.seqlens_k, a.cu_q, pl.batch,
+                       const_cast<int32_t*>(a.job_pref));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    grid = dim3(static_cast<unsigned>(static_cast<int64_t>(pl.batch) * pl.hk * a.maxc), 1, 1);
+  }
   if (pl.waves == 1) {
     if constexpr (T::KVB == 1) {
       if (uni)

@@ -41,6 +41,15 @@ struct AttnArgs {
   const void* v_new;
   void* k_store;
   void* v_store;
+  // One-wave decode kernels: when set, work item x of a one-dimensional grid
+  // takes the x-th job of a longest-first list -- every full 1024-key chunk of
+  // every (sequence, KV head) in (sequence, head, chunk) order, then the
+  // partial last chunks -- from the per-sequence prefix counts written by
+  // decode_plan_kernel: job_pref[b] = full chunks of sequences < b (b <= batch),
+  // job_pref[batch + 1 + b] = partial chunks of sequences < b.
+  const int32_t* job_pref;
+  int32_t nbatch;
+  int32_t nhk;
 };
 
 struct MergeArgs {
@@ -67,6 +76,7 @@ struct LaunchPlan {
   bool full;       // prefill kernel (true) or split kernels + merge (false)
   bool full4;      // full path, bf16/FP8: 4 waves x 32 columns (attn_kernel) instead of the 8-wave pipelined kernel
   bool full8;      // full path, bf16/FP8, no fused append: 8 waves x 32 columns (attn_kernel), one work group per CU
+  bool lpt;        // split path, one-wave kernels: longest-first job list (AttnArgs::job_pref)
   bool append;     // fused append of k_new / v_new
   bool skip_merge; // split path: write the chunk partials only
   int waves;       // split path: waves per work group (1 or 4)

@@ -96,7 +96,14 @@ def test_workspace_size_matches_partial_buffers():
     chunks = 4096 // pkv.CHUNK_KEYS
     parts = 64 * 16 * chunks
     want = -(-parts * 128 * 4 // 256) * 256 + -(-parts * 2 * 4 // 256) * 256
-    assert L.pkv_attn_workspace_size(ctypes.byref(lay)) == want
+    assert L.pkv_attn_workspace_size(ctypes.byref(lay)) == want   # 64 x 4 x 4 jobs: no job list
+    # 128 sequences x 8 KV heads x 8 chunks: the decode kernels' longest-first job list adds its prefix counts
+    lay2 = good_layout(max_seqlen_k=8192, total_q=128, batch=128, max_blocks_per_seq=512, num_heads_q=32,
+                       num_heads_k=8, k_block_stride=2 * 16 * 8 * 128, k_slot_stride=8 * 128,
+                       v_block_stride=2 * 16 * 8 * 128, v_slot_stride=8 * 128)
+    parts2 = 128 * 32 * 8
+    want2 = -(-parts2 * 128 * 4 // 256) * 256 + -(-parts2 * 2 * 4 // 256) * 256 + -(-(2 * 128 + 2) * 4 // 256) * 256
+    assert L.pkv_attn_workspace_size(ctypes.byref(lay2)) == want2
     assert L.pkv_attn_workspace_size(ctypes.byref(good_layout(head_dim=3))) == 0
 
 

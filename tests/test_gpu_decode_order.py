@@ -1,0 +1,94 @@
+"""The one-wave decode kernels' longest-first job list.
+
+With sequences spanning few chunks and more (sequence, KV head, chunk) jobs
+than one round of wave slots, the decode kernels take their work in a
+longest-first order (every full 1024-key chunk, then the partial last
+chunks), from prefix counts computed on the device.  A job is the same
+(sequence, KV head, chunk) as in the plain grid order, so the bits must not
+change: compared here with two chunks per work item (which keeps the plain
+order), with the full (prefill) path, and with the oracle on sampled
+sequences; the fused append under the same order against the unfused pair.
+"""
+
+from __future__ import annotations
+
+import math
+
+import pytest
+import torch
+
+import invariant_paged_kv_amd as pkv
+import pkv_inputs as gen
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def announce(msg: str) -> None:
+    print(f"[case] {msg}", flush=True)
+
+
+def ragged(seed, dtype, bs):
+    # 48 sequences x 8 KV heads x 8 chunks = 3072 job slots (> 2048): the job list is used
+    case = gc.make_case(seed, dtype if dtype != "fp8" else "bf16", 48, 32, 8, 128, bs, 8192,
+                        "interleaved", True, [1] * 48)
+    if dtype == "fp8":
+        g = torch.Generator().manual_seed(seed + 1)
+        nb = gen.pool_num_blocks(8192, bs, 48)
+        case.pool = gc.to_device(gen.new_pool(nb, bs, 8, 128, "fp8", "interleaved", generator=g))
+    # a mix of lengths: exact chunk multiples, one-key tails and one-key sequences
+    sl = list(case.seqlens)
+    sl[0], sl[1], sl[2], sl[3] = 1024, 1025, 1, 8192
+    case.seqlens = sl
+    return case
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("bs", [256, 24])
+def test_longest_first_order_keeps_bits(dtype, bs):
+    announce(f"decode job order {dtype} bs={bs}")
+    case = ragged(9700 + bs + (dtype == "fp8"), dtype, bs)
+    if dtype == "fp8":
+        from tests import test_gpu_fp8 as f8
+        case.extra = {"k_scale": 0.5, "v_scale": 1.25}
+        run = lambda **kw: f8.run(case, path=kw.get("path"), split=kw.get("split_chunks"))
+    else:
+        run = lambda **kw: gc.run(case, **kw)
+    out, lse = run()
+    gc.assert_bitwise(run(split_chunks=2), (out, lse), "plain order (2 chunks per item)")
+    gc.assert_bitwise(run(path=2), (out, lse), "full path")
+    if dtype == "fp8":
+        f8.check_oracle(case, out, lse, seq_ids=[0, 1, 2, 3, 17])
+    else:
+        gc.check_oracle(case, out, lse, seq_ids=[0, 1, 2, 3, 17])
+
+
+def test_longest_first_order_fused_append():
+    announce("decode job order, fused append")
+    case = ragged(9750, "bf16", 256)
+    B, HK, D = 48, 8, 128
+    g = torch.Generator().manual_seed(9751)
+    kn = gen.randn((B, HK, D), "bf16", generator=g).to(gc.DEV)
+    vn = gen.randn((B, HK, D), "bf16", generator=g).to(gc.DEV)
+    sk = torch.tensor(case.seqlens, dtype=torch.int32, device=gc.DEV)
+    cu = torch.arange(B + 1, dtype=torch.int32, device=gc.DEV)
+    # unfused: write the new rows, then attend (plain order via 2 chunks per item)
+    pk, pv = case.pool.k.clone(), case.pool.v.clone()
+    pkv.cache_write(kn, vn, pk, pv, case.block_table, sk - 1, cu)
+    with pkv.options(split_chunks=2):
+        ref = pkv.attn_forward(case.q, pk, pv, case.block_table, sk, cu, True, case.scale, max_seqlen_q=1,
+                               max_seqlen_k=8192, **gc.nan_outputs(case.q))
+    # fused, longest-first order
+    fk, fv = case.pool.k.clone(), case.pool.v.clone()
+    got = pkv.attn_forward_append(case.q, kn, vn, fk, fv, case.block_table, sk, cu, True, case.scale,
+                                  max_seqlen_q=1, max_seqlen_k=8192, **gc.nan_outputs(case.q))
+    torch.cuda.synchronize()
+    gc.assert_bitwise(got, ref, "fused append vs unfused")
+    assert torch.equal(fk.view(torch.int16), pk.view(torch.int16)) and torch.equal(fv.view(torch.int16), pv.view(torch.int16))
