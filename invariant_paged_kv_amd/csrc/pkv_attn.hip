@@ -8,11 +8,14 @@
 //                             loaded straight into registers a tile ahead.
 //   decode2_kernel            FP8 caches: the same with two tiles in flight.
 //   attn_kernel<SPLIT=true>   more columns (or fp32): 4 waves sharing LDS tiles.
+//   decode_plan_kernel        ragged batches: prefix counts for the one-wave
+//                             kernels' longest-first job order.
 // Full (prefill) path: one work item per (sequence, KV head, column block)
 // runs the chunks in ascending order, folds them in registers and makes the
 // final write.
-//   attn_kernel<SPLIT=false>  4 waves x 2 column groups, LDS tiles double-buffered
-//                             from a register stage.
+//   attn_kernel<SPLIT=false>  4 (or, for few columns per KV head over long
+//                             contexts, 8) waves x 2 column groups, LDS tiles
+//                             double-buffered from a register stage.
 //   prefill_kernel            the 8-wave x 16-column pipelined variant (kept as a
 //                             bitwise cross-check, PKV_OPT_FULL_KERNEL = 1).
 //
