@@ -92,3 +92,25 @@ def test_longest_first_order_fused_append():
     torch.cuda.synchronize()
     gc.assert_bitwise(got, ref, "fused append vs unfused")
     assert torch.equal(fk.view(torch.int16), pk.view(torch.int16)) and torch.equal(fv.view(torch.int16), pv.view(torch.int16))
+
+
+def test_longest_first_order_with_empty_sequences():
+    """Sequences without rows or without keys take no job; their rows get out = 0, lse = -inf."""
+    announce("decode job order, empty sequences")
+    B = 48
+    lens = [1] * B
+    for b in (5, 6, 30):          # no query rows
+        lens[b] = 0
+    case = gc.make_case(9760, "bf16", B, 32, 8, 128, 64, 8192, "interleaved", True, lens)
+    sl = list(case.seqlens)
+    for b in (7, 8, 47):          # rows but no keys
+        sl[b] = 0
+    sl[0], sl[9] = 1024, 1025
+    case.seqlens = sl
+    out, lse = gc.run(case)
+    gc.assert_bitwise(gc.run(case, split_chunks=2), (out, lse), "plain order")
+    gc.assert_bitwise(gc.run(case, path=2), (out, lse), "full path")
+    for b in (7, 8, 47):
+        r = case.cu[b]
+        assert torch.all(lse[r] == -math.inf) and torch.all(out[r] == 0), b
+    gc.check_oracle(case, out, lse, seq_ids=[0, 4, 7, 9, 31])
