@@ -16,6 +16,7 @@ library is not built, every call raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Tuple
 
@@ -235,6 +236,40 @@ def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                    _stream_handle(q.device))
     _check(rc, "pkv_attn_forward")
     return out, lse
+
+
+def flash_attn_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            cache_seqlens: torch.Tensor, page_table: torch.Tensor, causal: bool = False,
+                            softmax_scale: Optional[float] = None, return_softmax_lse: bool = False,
+                            k_scale: float = 1.0, v_scale: float = 1.0):
+    """The call shape of the pages' paged-cache interface, over ``attn_forward``.
+
+    aiter commit d293d61bbf19 ("pin non-contiguous paged KV block stride")
+    calls ``flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens=...,
+    page_table=..., causal=...)`` with batch-major queries ``q [B, Lq, Hq, d]``,
+    caches ``[num_blocks, block_size, Hkv, d]`` (views of an interleaved pool
+    allowed) and a page table ``[B, max_blocks]``; ``cache_seqlens[b]`` keys are
+    visible to sequence b and its Lq query rows are the last Lq positions
+    (bottom-right).  This packs q to ``[B * Lq, Hq, d]`` (a view), builds
+    ``cu_seqlens_q = [0, Lq, 2 Lq, ...]`` and calls ``attn_forward`` -- argument
+    marshalling only.  Returns ``out [B, Lq, Hq, d]``, and with
+    ``return_softmax_lse`` also ``lse [B, Hq, Lq]`` (natural log, fp32).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, seqlen_q, num_heads, head_dim]")
+    B, Lq, Hq, d = q.shape
+    qp = q.contiguous().view(B * Lq, Hq, d)
+    cu = torch.arange(0, B * Lq + 1, Lq, dtype=torch.int32, device=q.device) if Lq > 0 else \
+        torch.zeros(B + 1, dtype=torch.int32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    bs = k_cache.shape[1]
+    out, lse = attn_forward(qp, k_cache, v_cache, page_table, cache_seqlens, cu, causal, scale,
+                            max_seqlen_q=Lq, max_seqlen_k=page_table.shape[1] * bs,
+                            k_scale=k_scale, v_scale=v_scale)
+    out = out.view(B, Lq, Hq, d)
+    if return_softmax_lse:
+        return out, lse.view(B, Lq, Hq).permute(0, 2, 1)
+    return out
 
 
 def attn_forward_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
