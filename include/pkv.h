@@ -299,7 +299,9 @@ int pkv_validate_layout(const pkv_layout* kv_strides);
  * Process-wide tuning and test hooks.  None changes a result bit: they choose
  * which kernels run and how work is split.
  *   PKV_OPT_PATH          0 auto, 1 split (decode kernels + merge), 2 full (prefill kernel)
- *   PKV_OPT_SPLIT_CHUNKS  chunks handled by one split work item (0 = auto, 1..64)
+ *   PKV_OPT_SPLIT_CHUNKS  chunks handled by one split work item (0 = auto = 1, 1..64);
+ *                         with one chunk per item, ragged batches spanning at most 16
+ *                         chunks take the decode kernels' longest-first job order
  *   PKV_OPT_FULL_KERNEL   bf16/FP8 full path: 0 auto (3 when max_seqlen_q * Hq/Hkv <=
  *                         1024 and the keys reach 16384, else 2), 1 pipelined 8 waves x
  *                         16 columns per work group, 2 4 waves x 32 columns, 3 8 waves x
