@@ -11,8 +11,8 @@ Prints one JSON line: value = KV bytes read per second (GB/s) over the timed
 steps, the roofline of the attention launch (bytes it must move / its HIP-event
 duration vs 8 TB/s HBM), the oracle's throughput on a bounded sample of the
 same work on the host's cores, a prefill figure (TFLOP/s of the full causal
-prefill of batch 8 x 8192 tokens, Hq 16, Hkv 4) and of its backward, and
-bitwise checks.
+prefill of batch 8 x 8192 tokens, Hq 16, Hkv 4), of its backward and of the
+same prefill fed in 17- and 1024-token chunks, and bitwise checks.
 """
 
 from __future__ import annotations
@@ -211,7 +211,8 @@ def main():
     if not args.no_fp8:
         result["fp8_decode"] = bench_fp8_decode(torch, pkv, gen, B, N, args.steps, args.warmup, attn_avg_ms)
     if not args.no_prefill:
-        result["prefill"], result["backward"] = bench_prefill(torch, pkv, gen)
+        result["prefill"], result["backward"], chunked = bench_prefill(torch, pkv, gen)
+        result["chunked_prefill"] = chunked
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["oracle_parity"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale,
                                                                        out, lse)
@@ -328,6 +329,12 @@ def bench_prefill(torch, pkv, gen, reps: int = 5):
     # Algorithmic FLOPs: the five products dP, dV, dK, dQ and the recomputed S
     # over the causal pairs, 2.5x the forward's two.
     out, lse = call()
+    chunked = []
+    for c in (17, 1024):
+        try:
+            chunked.append(bench_chunked_prefill(torch, pkv, pool, bt, q, out, lse, S, scale, c))
+        except (RuntimeError, ValueError) as exc:   # reported in the line; the other figures still print
+            chunked.append({"chunk_tokens": c, "error": str(exc)[:200]})
     dout = gen.randn((B * S, HQ, D), "bf16", generator=g, device=dev)
     cuk = torch.arange(0, B * S + 1, S, dtype=torch.int32, device=dev)
     dq = torch.empty_like(q)
@@ -351,7 +358,102 @@ def bench_prefill(torch, pkv, gen, reps: int = 5):
                "tflops": round(btf, 2), "frac": round(btf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": bflops}
     del pool, out, lse, dout, dq, dk, dv
     torch.cuda.empty_cache()
-    return fwd, bwd_res
+    return fwd, bwd_res, chunked
+
+
+def bench_chunked_prefill(torch, pkv, pool, bt, q, ref_out, ref_lse, S, scale, chunk, reps: int = 3):
+    """The same prefill fed in chunks of `chunk` tokens per sequence.
+
+    Each call appends the chunk's K/V with pkv_cache_write (the bits the pool
+    already holds at those positions, so the cache is unchanged) and attends
+    the chunk's rows over every key up to the chunk's end.  The calls are
+    captured once as a HIP graph and replayed, as a serving loop would run
+    them; the chunked out/lse must equal the one-shot prefill's bit for bit.
+    """
+    dev = q.device
+    B, HK, D = bt.shape[0], pool.k.shape[2], pool.k.shape[3]
+    BS, HQ = pool.k.shape[1], q.shape[1]
+    used = bt[:, :S // BS].long()
+    kd = pool.k[used].reshape(B, S, HK, D)   # each sequence's keys and values, dense
+    vd = pool.v[used].reshape(B, S, HK, D)
+    qv = q.view(B, S, HQ, D)
+    calls = []
+    for lo in range(0, S, chunk):
+        hi = min(lo + chunk, S)
+        n = hi - lo
+        qc = qv[:, lo:hi].reshape(B * n, HQ, D).contiguous()
+        calls.append({
+            "lo": lo, "hi": hi, "q": qc,
+            "k": kd[:, lo:hi].reshape(B * n, HK, D).contiguous(),
+            "v": vd[:, lo:hi].reshape(B * n, HK, D).contiguous(),
+            "pos": torch.full((B,), lo, dtype=torch.int32, device=dev),
+            "sk": torch.full((B,), hi, dtype=torch.int32, device=dev),
+            "cu": torch.arange(0, B * n + 1, n, dtype=torch.int32, device=dev),
+            "out": torch.empty_like(qc),
+            "lse": torch.empty((B * n, HQ), dtype=torch.float32, device=dev),
+        })
+    del kd, vd
+    # the largest split-path workspace any call needs: B * chunk rows over all S keys
+    ws_bytes = pkv.workspace_size(q[:B * chunk], pool.k, pool.v, bt, max_seqlen_q=chunk, max_seqlen_k=S)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def run_all():
+        for c in calls:
+            pkv.cache_write(c["k"], c["v"], pool.k, pool.v, bt, c["pos"], c["cu"])
+            pkv.attn_forward(c["q"], pool.k, pool.v, bt, c["sk"], c["cu"], True, scale,
+                             max_seqlen_q=c["hi"] - c["lo"], max_seqlen_k=c["hi"], out=c["out"], lse=c["lse"],
+                             workspace=ws)
+
+    def same_as_one_shot():
+        ro, rl = ref_out.view(B, S, HQ, D), ref_lse.view(B, S, HQ)
+        ok = True
+        for c in calls:
+            n = c["hi"] - c["lo"]
+            ok = ok and torch.equal(c["out"].view(B, n, HQ, D).view(torch.int16),
+                                    ro[:, c["lo"]:c["hi"]].view(torch.int16))
+            ok = ok and torch.equal(c["lse"].view(B, n, HQ).view(torch.int32), rl[:, c["lo"]:c["hi"]].view(torch.int32))
+        return bool(ok)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        run_all()                      # eager pass on the capture stream
+        torch.cuda.synchronize()
+        eager_same = same_as_one_shot()
+        with torch.cuda.graph(graph, stream=side):
+            run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for c in calls:
+        c["out"].fill_(float("nan"))
+        c["lse"].fill_(float("nan"))
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    replay_same = same_as_one_shot()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    timed_same = same_as_one_shot()
+    flops = 4.0 * D * HQ * B * (S * (S + 1) / 2)
+    kv_bytes = sum(B * c["hi"] * HK * D * 2 * 2 for c in calls)   # every call re-reads the keys it sees
+    res = {"workload": f"the same prefill in {len(calls)} chunks of {chunk} tokens per sequence "
+                       "(cache_write + attention per chunk, replayed as one HIP graph)",
+           "chunk_tokens": chunk, "calls": len(calls), "ms": round(ms, 3),
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "kv_reread_bytes": kv_bytes, "kv_GBs": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+           "hbm_frac": round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "bitwise_eq_one_shot": eager_same and replay_same and timed_same}
+    del graph, calls, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, out, lse, budget_s: float = 12.0):
