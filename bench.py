@@ -89,28 +89,32 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    # one pair of events per timed step around the attention call, read after
+    # the timed region: the steps are enqueued back to back, as a decode loop
+    # would run them
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i=None):
         pkv.cache_write(kn, vn, pool.k, pool.v, bt, pos, cu)
-        ev0.record(stream)
+        if i is not None:
+            evs[i][0].record(stream)
         pkv.attn_forward(q, pool.k, pool.v, bt, seqlens, cu, True, scale, max_seqlen_q=1, max_seqlen_k=N,
                          out=out, lse=lse, workspace=ws)
-        ev1.record(stream)
+        if i is not None:
+            evs[i][1].record(stream)
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    attn_ms = 0.0
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-        ev1.synchronize()
-        attn_ms += ev0.elapsed_time(ev1)
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    attn_avg_ms = attn_ms / args.steps
+    attn_avg_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ev0 = torch.cuda.Event(enable_timing=True)   # for the one-call timings below
+    ev1 = torch.cuda.Event(enable_timing=True)
 
     kv_bytes = B * N * HK * D * 2 * 2
     attn_bytes = kv_bytes + 2 * q.numel() * 2 + lse.numel() * 4 + B * math.ceil(N / BS) * 4 + 2 * (B + 1) * 4

@@ -952,12 +952,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int part = static_cast<int>(wg % WPR);
   if (w >= a.total_q * a.hq) return;
   const int64_t row = w / a.hq;
-  int lo = 0, hi = a.batch;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.cu_q[mid] <= row) lo = mid; else hi = mid - 1;
-  }
-  const int b = lo;
+  const int b = row_sequence(a.cu_q, a.batch, row);
   if (b >= a.batch) return;
   const int n = a.seqlens_k[b];
   const int L = a.cu_q[b + 1] - a.cu_q[b];

@@ -14,32 +14,38 @@ namespace pkv {
 typedef uint32_t u32x4_cw __attribute__((ext_vector_type(4)));
 
 // One work group per new token; threads copy 16-byte pieces of the token's
-// K and V rows (all KV heads).
+// K and V rows (all KV heads).  A thread's first piece is loaded before the
+// token's position is looked up (its source does not depend on it), so the
+// lookup's loads and the row's load are in flight together.
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int eb) {
   const int64_t tok = blockIdx.x;
-  int lo = 0, hi = a.batch;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.cu_new[mid] <= tok) lo = mid; else hi = mid - 1;
-  }
-  const int b = lo;
+  const int cpr = a.row_bytes / 16;
+  const int per_tensor = a.hk * cpr;
+  const int npieces = 2 * per_tensor;
+  auto src_of = [&](int i) {
+    const int tensor = i / per_tensor;
+    const int rem = i - tensor * per_tensor;
+    return static_cast<const unsigned char*>(tensor ? a.v_new : a.k_new) + (tok * a.hk + rem / cpr) * a.row_bytes +
+           16 * (rem % cpr);
+  };
+  const int i0 = static_cast<int>(threadIdx.x);
+  u32x4_cw first = {0, 0, 0, 0};
+  if (i0 < npieces) first = *reinterpret_cast<const u32x4_cw*>(src_of(i0));
+  const int b = row_sequence(a.cu_new, a.batch, tok);
   if (b >= a.batch) return;
   const int pos = a.seqlens_k[b] + static_cast<int>(tok - a.cu_new[b]);
   const int bi = div_block(pos, a.bs_mul, a.bs_shift);
   const int64_t blk = a.block_table[(int64_t)b * a.mbps + bi];
   const int64_t slot = pos - bi * a.bs;
-  const int cpr = a.row_bytes / 16;
-  const int per_tensor = a.hk * cpr;
-  for (int i = threadIdx.x; i < 2 * per_tensor; i += blockDim.x) {
+  for (int i = i0; i < npieces; i += blockDim.x) {
     const int tensor = i / per_tensor;
     const int rem = i - tensor * per_tensor;
     const int h = rem / cpr;
     const int part = rem - h * cpr;
-    const unsigned char* src = static_cast<const unsigned char*>(tensor ? a.v_new : a.k_new) +
-                               (tok * a.hk + h) * a.row_bytes + 16 * part;
+    const u32x4_cw val = i == i0 ? first : *reinterpret_cast<const u32x4_cw*>(src_of(i));
     const int64_t off = tensor ? (blk * a.vbs + slot * a.vss + h * a.vhs) : (blk * a.kbs + slot * a.kss + h * a.khs);
     unsigned char* dst = static_cast<unsigned char*>(tensor ? a.v_cache : a.k_cache) + off * eb + 16 * part;
-    *reinterpret_cast<u32x4_cw*>(dst) = *reinterpret_cast<const u32x4_cw*>(src);
+    *reinterpret_cast<u32x4_cw*>(dst) = val;
   }
 }
 

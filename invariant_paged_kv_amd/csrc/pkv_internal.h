@@ -115,6 +115,26 @@ __device__ __forceinline__ int div_block(int j, uint32_t mul, int shift) {
   return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(j)) * mul) >> shift);
 }
 
+// The sequence of packed row `row`: the largest b in [0, batch] with
+// cu[b] <= row (cu nondecreasing from cu[0] = 0, so rows at or past
+// cu[batch] give batch).  A 64-way search by the whole wave (row must be the
+// same in every lane and every lane active): each round the lanes probe 64
+// evenly spaced offsets and a ballot counts those <= row, so batches of up to
+// 64 sequences take one round of loads, up to 4096 two, instead of one
+// dependent load per halving.
+__device__ __forceinline__ int row_sequence(const int32_t* cu, int batch, int64_t row) {
+  int lo = 0, hi = batch;
+  while (lo < hi) {
+    const int stride = (hi - lo + 63) >> 6;
+    const int p = lo + (static_cast<int>(__lane_id()) + 1) * stride;
+    const bool le = p <= hi && cu[p] <= row;
+    const int c = __popcll(__ballot(le));
+    hi = min(hi, lo + (c + 1) * stride - 1);
+    lo += c * stride;
+  }
+  return lo;
+}
+
 // Arguments of the backward kernels.  `f` carries the forward's inputs
 // (q, caches, table, lengths, strides, GQA factor, block-size divisor,
 // causal flag; f.mul is the score multiplier of the forward).
