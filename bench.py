@@ -365,7 +365,8 @@ def bench_prefill(torch, pkv, gen, reps: int = 5):
     return fwd, bwd_res, chunked
 
 
-def bench_chunked_prefill(torch, pkv, pool, bt, q, ref_out, ref_lse, S, scale, chunk, reps: int = 3):
+def bench_chunked_prefill(torch, pkv, pool, bt, q, ref_out, ref_lse, S, scale, chunk, reps: int = 3,
+                          fused: bool = False):
     """The same prefill fed in chunks of `chunk` tokens per sequence.
 
     Each call appends the chunk's K/V with pkv_cache_write (the bits the pool
@@ -373,6 +374,7 @@ def bench_chunked_prefill(torch, pkv, pool, bt, q, ref_out, ref_lse, S, scale, c
     the chunk's rows over every key up to the chunk's end.  The calls are
     captured once as a HIP graph and replayed, as a serving loop would run
     them; the chunked out/lse must equal the one-shot prefill's bit for bit.
+    With `fused`, each call is one pkv_attn_forward_append instead.
     """
     dev = q.device
     B, HK, D = bt.shape[0], pool.k.shape[2], pool.k.shape[3]
@@ -403,6 +405,11 @@ def bench_chunked_prefill(torch, pkv, pool, bt, q, ref_out, ref_lse, S, scale, c
 
     def run_all():
         for c in calls:
+            if fused:
+                pkv.attn_forward_append(c["q"], c["k"], c["v"], pool.k, pool.v, bt, c["sk"], c["cu"], True, scale,
+                                        max_seqlen_q=c["hi"] - c["lo"], max_seqlen_k=c["hi"], out=c["out"],
+                                        lse=c["lse"], workspace=ws)
+                continue
             pkv.cache_write(c["k"], c["v"], pool.k, pool.v, bt, c["pos"], c["cu"])
             pkv.attn_forward(c["q"], pool.k, pool.v, bt, c["sk"], c["cu"], True, scale,
                              max_seqlen_q=c["hi"] - c["lo"], max_seqlen_k=c["hi"], out=c["out"], lse=c["lse"],

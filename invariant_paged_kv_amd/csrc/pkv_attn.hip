@@ -65,6 +65,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #ifndef PKV_FULL_DB
 #define PKV_FULL_DB 1
 #endif
+#ifndef PKV_SPLIT_LATE_COMMIT
+#define PKV_SPLIT_LATE_COMMIT 1
+#endif
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND, bool U>
 __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a) {
@@ -81,6 +84,13 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
   // jmax - 1, so the extra loads stay in bounds.
   constexpr bool kPrefetch = PKV_FULL_PREFETCH && T::EB == 2 && (W == 4 || W == 8) && !APPEND;
   constexpr bool kDouble = kPrefetch && PKV_FULL_DB;
+  // Split kernel (no running fold state, so registers to spare): the staged
+  // tile t+1 is written into the idle LDS buffer between the softmax and the
+  // P.V products of tile t, right before tile t+2's loads are issued into the
+  // same registers, so its loads have a whole tile to land instead of the
+  // second half of one.  The buffer is free there: every wave passed the
+  // barrier that ended tile t-1, its last reader.
+  constexpr bool kLateCommit = kDouble && SPLIT && PKV_SPLIT_LATE_COMMIT;
   __shared__ __attribute__((aligned(16))) unsigned char lds[(kDouble ? 2 : 1) * G_::BYTES];
   unsigned char* k_lds = lds;
   unsigned char* v_lds = lds + G_::KBYTES;
@@ -180,8 +190,10 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
         if constexpr (kDouble) {
           // tile j0 is in buffer (j0 / KT) & 1; the other one is free: stage tile j0 + KT there
           const int cur = (j0 / KT) & 1;
-          unsigned char* const nk = lds + (cur ^ 1) * G_::BYTES;
-          tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, stg, nk, nk + G_::KBYTES, ap);
+          if constexpr (!kLateCommit) {
+            unsigned char* const nk = lds + (cur ^ 1) * G_::BYTES;
+            tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, stg, nk, nk + G_::KBYTES, ap);
+          }
           k_lds = lds + cur * G_::BYTES;
           v_lds = k_lds + G_::KBYTES;
         } else {
@@ -208,7 +220,13 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
           const int jn = kDouble ? j0 + 2 * KT : j0 + KT;
           // V operands two P.V steps ahead where registers allow (scalar block ids)
           softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0, true, U ? 2 : 1>(
-              st, s, lim, j0, a.mul, v_lds, [&] { tile_issue<T, D, W, APPEND, U>(a, bt, hk, jn, jmax, stg, ap); });
+              st, s, lim, j0, a.mul, v_lds, [&] {
+                if constexpr (kLateCommit) {
+                  unsigned char* const nk = lds + (((j0 / KT) & 1) ^ 1) * G_::BYTES;
+                  tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, stg, nk, nk + G_::KBYTES, ap);
+                }
+                tile_issue<T, D, W, APPEND, U>(a, bt, hk, jn, jmax, stg, ap);
+              });
         } else {
           softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
         }
