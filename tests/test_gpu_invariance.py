@@ -69,6 +69,21 @@ def test_full_path_kernels_agree(layout):
     gc.assert_bitwise(gc.run(case, path=1), ref, "split vs full")
 
 
+def test_chunked_prefill_rows_split_kernel():
+    """17-row chunks of a GQA-4 group (68 columns per KV head, the 4-wave split
+    kernel, whose staged tiles cross chunk boundaries inside a work item when it
+    takes several chunks) over contexts of one to five 1024-key chunks: every
+    grouping of chunks into work items and the full path give the same bits."""
+    announce("chunked-prefill rows, split kernel")
+    lens, seqlens = [17, 17, 17, 17], [4100, 2049, 1041, 17]
+    case = gc.make_case(3020, "bf16", 4, 16, 4, 128, 16, max(seqlens), "contiguous", True, lens, seqlens)
+    ref = gc.run(case, path=1)
+    gc.check_oracle(case, *ref, seq_ids=[1, 3])
+    for split in (2, 3, 5):
+        gc.assert_bitwise(gc.run(case, path=1, split_chunks=split), ref, f"split {split}")
+    gc.assert_bitwise(gc.run(case, path=2), ref, "full path")
+
+
 def test_permuted_block_table():
     announce("permuted block table")
     case = mixed_case(seed=3002, layout="contiguous")
