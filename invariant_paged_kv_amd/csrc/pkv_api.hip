@@ -170,6 +170,14 @@ Plan make_plan(const pkv_layout& l, bool append = false) {
   const int64_t jobs = static_cast<int64_t>(l.batch) * l.num_heads_k * p.maxc;
   p.lp.lpt = PKV_DECODE_LPT && !full && waves == 1 && l.dtype != PKV_F32 && p.cpi == 1 && p.maxc <= 16 &&
              jobs > 2048 && jobs <= INT32_MAX;
+  // One-wave bf16 decode: the two-stage kernel (two tiles in flight, 416
+  // registers, one wave per SIMD; same bits) once the grid exceeds one round
+  // of one-wave slots (256 CUs x 4 SIMDs).  In-process A/B against the
+  // one-stage kernel (two waves per SIMD): 128 ragged sequences of up to 8192
+  // keys 0.407 -> 0.393 ms, 16 x 131072 keys 1.484 -> 1.476 ms; 64 x 4096
+  // keys (1024 work items) 0.108 -> 0.110, hence the condition.
+  p.lp.two_stage = !full && waves == 1 && l.dtype == PKV_BF16 &&
+                   static_cast<int64_t>(p.lp.items) * l.num_heads_k * l.batch > 1024;
   p.lp.batch = l.batch;
   p.lp.hk = l.num_heads_k;
   p.lp.total_q = l.total_q;

@@ -6,7 +6,8 @@
 // the final write.
 //   decode_kernel             bf16, up to 16 columns per KV head: one wave, K/V
 //                             loaded straight into registers a tile ahead.
-//   decode2_kernel            FP8 caches: the same with two tiles in flight.
+//   decode2_kernel            the same with two tiles in flight: FP8 caches,
+//                             and bf16 when the grid exceeds 1024 work items.
 //   attn_kernel<SPLIT=true>   more columns (or fp32): 4 waves sharing LDS tiles.
 //   decode_plan_kernel        ragged batches: prefix counts for the one-wave
 //                             kernels' longest-first job order.
@@ -882,7 +883,7 @@ __device__ __forceinline__ void decode2_tile(const AttnArgs& a, const int32_t* b
 }
 
 template <class T, int D, bool APPEND, bool U>
-__global__ __launch_bounds__(64, 2) void decode2_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64, T::KVB == 1 ? 2 : 1) void decode2_kernel(AttnArgs a) {
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
 
@@ -1059,13 +1060,19 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
     grid = dim3(static_cast<unsigned>(static_cast<int64_t>(pl.batch) * pl.hk * a.maxc), 1, 1);
   }
   if (pl.waves == 1) {
+    // FP8 always, bf16 when the grid exceeds one round of one-wave slots:
+    // the two-stage kernel (two tiles in flight, one wave per SIMD)
     if constexpr (T::KVB == 1) {
       if (uni)
         hipLaunchKernelGGL((decode2_kernel<T, D, APPEND, true>), grid, dim3(64), 0, stream, a);
       else
         hipLaunchKernelGGL((decode2_kernel<T, D, APPEND, false>), grid, dim3(64), 0, stream, a);
     } else if constexpr (T::EB == 2) {
-      if (uni)
+      if (pl.two_stage && uni)
+        hipLaunchKernelGGL((decode2_kernel<T, D, APPEND, true>), grid, dim3(64), 0, stream, a);
+      else if (pl.two_stage)
+        hipLaunchKernelGGL((decode2_kernel<T, D, APPEND, false>), grid, dim3(64), 0, stream, a);
+      else if (uni)
         hipLaunchKernelGGL((decode_kernel<T, D, APPEND, true>), grid, dim3(64), 0, stream, a);
       else
         hipLaunchKernelGGL((decode_kernel<T, D, APPEND, false>), grid, dim3(64), 0, stream, a);

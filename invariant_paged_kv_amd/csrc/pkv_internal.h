@@ -77,6 +77,7 @@ struct LaunchPlan {
   bool full4;      // full path, bf16/FP8: 4 waves x 32 columns (attn_kernel) instead of the 8-wave pipelined kernel
   bool full8;      // full path, bf16/FP8, no fused append: 8 waves x 32 columns (attn_kernel), one work group per CU
   bool lpt;        // split path, one-wave kernels: longest-first job list (AttnArgs::job_pref)
+  bool two_stage;  // split path, one-wave bf16 kernel: two tiles in flight (decode2_kernel)
   bool append;     // fused append of k_new / v_new
   bool skip_merge; // split path: write the chunk partials only
   int waves;       // split path: waves per work group (1 or 4)
