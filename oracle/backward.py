@@ -116,6 +116,29 @@ def attention_backward(q: np.ndarray, k_flat: np.ndarray, v_flat: np.ndarray,
     return dq, dk, dv
 
 
+def head_bound(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray,
+               vis: np.ndarray, softmax_scale: float):
+    """Term bounds of one head of one sequence: ``(Aq [L,d], Ak [n,d], Av [n,d])``.
+
+    With ``G[i, j] = sum_e |dO[i, e]| |V[j, e]|`` (a bound of ``|dP[i, j]|``)
+    and ``F[i] = sum_j P[i, j] G[i, j]`` (a bound of the row term)::
+
+        Aq[i] = |scale| * sum_j P[i, j] (G[i, j] + F[i]) |K[j]|
+        Ak[j] = |scale| * sum_i P[i, j] (G[i, j] + F[i]) |Q[i]|
+        Av[j] = sum_i P[i, j] |dO[i]|
+
+    Expanding dS into its monomials (``P dO V`` and ``P P dO V``), each bound
+    is exactly the sum of the absolute values of the monomials its gradient
+    element adds up.
+    """
+    P, _ = masked_softmax(scores(Q, K, softmax_scale), vis)
+    G = np.abs(dO) @ np.abs(V).T
+    F = np.sum(P * G, axis=1)
+    W = P * (G + F[:, None])
+    return (abs(softmax_scale) * (W @ np.abs(K)), abs(softmax_scale) * (W.T @ np.abs(Q)),
+            P.T @ np.abs(dO))
+
+
 def attention_backward_bound(q: np.ndarray, k_flat: np.ndarray, v_flat: np.ndarray,
                              layout: Layout, block_table: np.ndarray,
                              seqlens_k: Sequence[int], cu_seqlens_q: Sequence[int],
@@ -124,25 +147,18 @@ def attention_backward_bound(q: np.ndarray, k_flat: np.ndarray, v_flat: np.ndarr
     """Magnitude of the terms each gradient element sums, for error bounds.
 
     The same formulas as ``attention_backward`` with every quantity replaced by
-    an upper bound of its absolute value: ``G[i, j] = sum_e |dO[i, e]| |V[j, e]|``
-    bounds ``|dP[i, j]|``; ``F[i] = sum_j P[i, j] G[i, j]`` bounds both the row
-    term and ``sum_e |dO[i, e]| |out[i, e]|``; then
-
-        Aq[i, h]  = scale * sum_j P[i, j] (G[i, j] + F[i]) |K[j]|
-        Ak[j, hk] = scale * sum_i P[i, j] (G[i, j] + F[i]) |Q[i, h]|   (summed over h)
-        Av[j, hk] = sum_i P[i, j] |dO[i]|                              (summed over h)
-
-    By the triangle inequality each gradient's absolute value is at most its
-    bound, and the rounding error of any evaluation that rounds its operands
-    and sums in finite precision is a small multiple of the unit roundoff times
-    the bound (the usual forward error analysis of a dot product).
+    an upper bound of its absolute value (``head_bound``), the heads of a GQA
+    group adding up in ``Ak``/``Av`` as their gradients do.  By the triangle
+    inequality each gradient's absolute value is at most its bound, and the
+    rounding error of any evaluation that rounds its operands and sums in
+    finite precision is a small multiple of the unit roundoff times the bound
+    (the usual forward error analysis of a dot product).
     """
     Hq, Hk, d = layout.num_heads_q, layout.num_heads_k, layout.head_dim
-    qf = np.abs(_as_f64(q, layout.dtype).reshape(-1, Hq, d))
-    dof = np.abs(_as_f64(dout, layout.dtype).reshape(-1, Hq, d))
     qs = _as_f64(q, layout.dtype).reshape(-1, Hq, d)
+    dof = _as_f64(dout, layout.dtype).reshape(-1, Hq, d)
     cuk = cu_seqlens_k_of(seqlens_k)
-    aq = np.zeros_like(qf)
+    aq = np.zeros_like(qs)
     ak = np.zeros((int(cuk[-1]), Hk, d), dtype=np.float64)
     av = np.zeros_like(ak)
     for b, r0, r1, n, K, V, vis in _sequences(q, k_flat, v_flat, layout, block_table,
@@ -152,11 +168,8 @@ def attention_backward_bound(q: np.ndarray, k_flat: np.ndarray, v_flat: np.ndarr
         k0 = int(cuk[b])
         for h in range(Hq):
             hk = kv_head_of(h, Hq, Hk)
-            P, _ = masked_softmax(scores(qs[r0:r1, h], K[:, hk], softmax_scale), vis)
-            G = dof[r0:r1, h] @ np.abs(V[:, hk]).T
-            F = np.sum(P * G, axis=1)
-            W = P * (G + F[:, None])
-            aq[r0:r1, h] = abs(softmax_scale) * (W @ np.abs(K[:, hk]))
-            ak[k0:k0 + n, hk] += abs(softmax_scale) * (W.T @ qf[r0:r1, h])
-            av[k0:k0 + n, hk] += P.T @ dof[r0:r1, h]
+            bq, bk, bv = head_bound(qs[r0:r1, h], K[:, hk], V[:, hk], dof[r0:r1, h], vis, softmax_scale)
+            aq[r0:r1, h] = bq
+            ak[k0:k0 + n, hk] += bk
+            av[k0:k0 + n, hk] += bv
     return aq, ak, av

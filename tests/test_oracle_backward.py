@@ -14,16 +14,21 @@ It is checked against things other than itself:
 * the pages' invariances: GQA equals MHA on repeated K/V (summed over the
   group), a decode row's dq equals the same row's dq in a causal prefill,
   interleaved equals contiguous, fully masked rows have zero gradients;
-* the error bound: every gradient's magnitude is at most its term bound.
+* the error bound: every gradient's magnitude is at most its term bound, and
+  the term bound equals the sum of the absolute values of the monomials of
+  the chain-rule expansion, enumerated one by one in 40-digit decimal
+  arithmetic (so an inflated bound fails as well as a deflated one).
 
 ``test_planted_backward_mistakes_are_caught`` plants plausible mistakes in
 the oracle (the row term dropped, the scale dropped from dq, P used where dS
-belongs, dS used where P belongs, the GQA map taken modulo) and checks that
-the pins fail.
+belongs, dS used where P belongs, the GQA map taken modulo; and in the term
+bound: the scale dropped, the row-term bound F counted twice, a stray factor
+of the group size) and checks that the pins fail.
 """
 
 from __future__ import annotations
 
+import decimal
 import math
 
 import numpy as np
@@ -260,9 +265,97 @@ def check_bound():
                 assert np.all(np.abs(r) <= a * (1 + 1e-12) + 1e-300)
 
 
+def _nested(t):
+    return t.to(torch.float64).tolist()
+
+
+def brute_force_bound(q, pool, bt, seqlens, cu, causal, scale, dout):
+    """Term bounds by enumeration, in 40-digit decimal arithmetic.
+
+    Expanding the chain rule down to the softmax weights P, every gradient
+    element is a sum of monomials:
+
+        dq[i, h, e]  =  scale * sum_j sum_f P_ij dO_if V_jf K_je
+                      - scale * sum_j sum_k sum_f P_ij P_ik dO_if V_kf K_je
+        dk[j, hk, e] =  scale * sum_(h, i) sum_f P_ij dO_if V_jf Q_ie
+                      - scale * sum_(h, i) sum_k sum_f P_ij P_ik dO_if V_kf Q_ie
+        dv[j, hk, e] =  sum_(h, i) P_ij dO_ie
+
+    (h runs over the query heads of KV head hk).  The bound of an element is
+    the sum of the absolute values of its monomials, enumerated one by one
+    here.  P is computed from its definition (exp of the scaled score over the
+    sum of exps of the row's visible keys, no max subtraction); K/V are read
+    from a nested-list copy of the pool through the block table.
+    """
+    ctx = decimal.Context(prec=40)
+    D = decimal.Decimal
+    Kp, Vp, Q, dO = _nested(pool.k), _nested(pool.v), _nested(q), _nested(dout)
+    hq, d = q.shape[1], q.shape[2]
+    hk_n, bs = pool.k.shape[2], pool.k.shape[1]
+    g = hq // hk_n
+    table = bt.tolist()
+    cuk = [0]
+    for n in seqlens:
+        cuk.append(cuk[-1] + n)
+    aq = [[[D(0)] * d for _ in range(hq)] for _ in range(q.shape[0])]
+    ak = [[[D(0)] * d for _ in range(hk_n)] for _ in range(cuk[-1])]
+    av = [[[D(0)] * d for _ in range(hk_n)] for _ in range(cuk[-1])]
+    sc = abs(D(scale))
+    for b, n in enumerate(seqlens):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        L = r1 - r0
+
+        def kv(tab, j, hk, e):
+            return D(tab[table[b][j // bs]][j % bs][hk][e])
+
+        for r in range(L):
+            i = r0 + r
+            J = [j for j in range(n) if not causal or j <= n - L + r]
+            if not J:
+                continue
+            for h in range(hq):
+                hk = h // g
+                ex = {j: ctx.exp(D(scale) * sum((D(Q[i][h][e]) * kv(Kp, j, hk, e) for e in range(d)), D(0)))
+                      for j in J}
+                z = sum(ex.values(), D(0))
+                P = {j: ex[j] / z for j in J}
+                for e in range(d):
+                    tq = D(0)
+                    for j in J:
+                        for f in range(d):
+                            tq += abs(P[j] * D(dO[i][h][f]) * kv(Vp, j, hk, f) * kv(Kp, j, hk, e))
+                            for k in J:
+                                tq += abs(P[j] * P[k] * D(dO[i][h][f]) * kv(Vp, k, hk, f) * kv(Kp, j, hk, e))
+                    aq[i][h][e] += sc * tq
+                    for j in J:
+                        tk = D(0)
+                        for f in range(d):
+                            tk += abs(P[j] * D(dO[i][h][f]) * kv(Vp, j, hk, f) * D(Q[i][h][e]))
+                            for k in J:
+                                tk += abs(P[j] * P[k] * D(dO[i][h][f]) * kv(Vp, k, hk, f) * D(Q[i][h][e]))
+                        ak[cuk[b] + j][hk][e] += sc * tk
+                        av[cuk[b] + j][hk][e] += abs(P[j] * D(dO[i][h][e]))
+    to = lambda x: np.array([[[float(v) for v in row] for row in m] for m in x]).reshape(len(x), -1, d)
+    return to(aq), to(ak), to(av)
+
+
+def check_bound_brute_force():
+    """The oracle's term bound equals the enumerated sum of |monomials| (two-sided pin)."""
+    for seed, dt, hq, hk, lens, sl, causal, scale in ((181, "f32", 4, 2, (2, 3), [5, 6], True, 0.4),
+                                                      (182, "bf16", 4, 1, (3, 1), [4, 6], False, 0.7),
+                                                      (183, "f32", 2, 2, (3, 2), [2, 5], True, 1.3)):
+        q, pool, bt, seqlens, cu, dout = case(seed, dt, "interleaved", 2, hq, hk, 3, 2, 6, lens, seqlens=sl)
+        got = oracle_backward(q, pool, bt, seqlens, cu, causal, scale, dout, bound=True)
+        want = brute_force_bound(q, pool, bt, seqlens, cu, causal, scale, dout)
+        for name, a, w in zip(("Aq", "Ak", "Av"), got, want):
+            assert a.shape == w.shape, (name, a.shape, w.shape)
+            err = float(np.max(np.abs(a - w) / np.maximum(np.abs(w), 1e-300)))
+            assert err <= 1e-12, f"{name} bound vs enumerated monomials (seed {seed}): rel err {err:.3e}"
+
+
 PINS = [check_torch_autograd, check_finite_differences, check_softmax_identities, check_closed_forms,
         check_gqa_equals_repeated_mha, check_decode_row_dq_equals_prefill_row, check_layout_and_masking,
-        check_bound]
+        check_bound, check_bound_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -295,19 +388,44 @@ def _grads_with(mistake):
     return head_gradients
 
 
+def _bound_with(mistake):
+    """Inflated term bounds: the scale dropped, F counted twice, a stray factor g."""
+    def head_bound(Q, K, V, dO, vis, softmax_scale):
+        P, _ = oracle.masked_softmax(oracle.scores(Q, K, softmax_scale), vis)
+        G = np.abs(dO) @ np.abs(V).T
+        F = np.sum(P * G, axis=1)
+        W = P * (G + (2 if mistake == "F_twice" else 1) * F[:, None])
+        s = 1.0 if mistake == "no_scale" else abs(softmax_scale)
+        return s * (W @ np.abs(K)), s * (W.T @ np.abs(Q)), P.T @ np.abs(dO)
+
+    if mistake != "extra_g":
+        return head_bound
+    real = ob.attention_backward_bound
+
+    def attention_backward_bound(q, k_flat, v_flat, layout, *args):
+        aq, ak, av = real(q, k_flat, v_flat, layout, *args)
+        g = layout.num_heads_q // layout.num_heads_k
+        return aq, g * ak, g * av
+    return attention_backward_bound
+
+
 MISTAKES = {
     "no_row_term": ("head_gradients", _grads_with("no_row_term")),
     "dq_no_scale": ("head_gradients", _grads_with("dq_no_scale")),
     "dk_uses_P": ("head_gradients", _grads_with("dk_uses_P")),
     "dv_uses_dS": ("head_gradients", _grads_with("dv_uses_dS")),
     "gqa_modulo": ("kv_head_of", lambda h, hq, hk: h % hk),
+    "bound_no_scale": ("head_bound", _bound_with("no_scale")),
+    "bound_F_twice": ("head_bound", _bound_with("F_twice")),
+    "bound_extra_g": ("attention_backward_bound", _bound_with("extra_g")),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MISTAKES))
 def test_planted_backward_mistakes_are_caught(name, monkeypatch):
     attr, fn = MISTAKES[name]
-    monkeypatch.setattr(ob, attr, fn)
+    # the test bridge calls the bound through the package namespace
+    monkeypatch.setattr(oracle if attr == "attention_backward_bound" else ob, attr, fn)
     failed = []
     for pin in PINS:
         try:
