@@ -559,9 +559,16 @@ __device__ __forceinline__ FoldCoef<T> fold_coef(float M, float mc) {
 __device__ __forceinline__ float fold_val(float acc, float a, float x, float b) { return fmaf(acc, a, x * b); }
 
 // Final write: out = O / L rounded once to the output type; lse in natural log.
+// fp32: M + ln L evaluated in double and rounded once to fp32, so the final
+// step adds at most half an fp32 ulp of the result (in fp32, logf's error and
+// the rounding of the sum came on top of it: 1.06e-6 at a 5000-key LSE near 9,
+// where the ulp is 9.5e-7).  Every kernel's final write calls this, so the
+// decode and prefill paths keep the same bits.
 template <class T>
 __device__ __forceinline__ float final_lse(float M, float L) {
-  return M == -INFINITY ? -INFINITY : pkv_lse<T>(M, L);
+  if (M == -INFINITY) return -INFINITY;
+  if constexpr (T::kBase2) return pkv_lse<T>(M, L);
+  else return static_cast<float>(static_cast<double>(M) + log(static_cast<double>(L)));
 }
 // vs: the stored-V scale (1 for unscaled caches: the multiply is then exact).
 __device__ __forceinline__ float final_val(float M, float O, float L, float vs) {
