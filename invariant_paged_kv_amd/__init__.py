@@ -25,6 +25,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_ALIGN, PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_OPTION = \
+    0, -1, -2, -3, -4, -5, -6, -7
 PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL = 1, 2, 3
 CHUNK_KEYS = 1024
 TILE_KEYS = 64
@@ -166,6 +168,8 @@ def make_layout(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch
         raise ValueError("the head-dim stride of k_cache and v_cache must be 1")
     if k_cache.dtype != v_cache.dtype:
         raise TypeError("k_cache and v_cache dtypes differ")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [batch, max_blocks_per_seq]")
     nb, bs, hk, d = k_cache.shape
     L = PkvLayout()
     L.dtype = _dtype_code(k_cache.dtype)
@@ -196,6 +200,58 @@ def _int32(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+# Argument checks.  The C ABI receives raw addresses and cannot see a tensor's
+# device or size, so an undersized buffer or a host tensor would become an
+# out-of-bounds or host-pointer access inside a kernel; every public call
+# checks shapes and dtypes first, then devices, before the library is touched.
+
+def _check_index(block_table: torch.Tensor, seqlens_k: torch.Tensor, cu: torch.Tensor, cu_name: str) -> int:
+    """int32 block table [batch, max_blocks], seqlens [batch], cumulative lengths [batch + 1]; returns batch."""
+    _int32(block_table, "block_table")
+    _int32(seqlens_k, "seqlens_k")
+    _int32(cu, cu_name)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+    batch = block_table.shape[0]
+    if seqlens_k.dim() != 1 or seqlens_k.numel() != batch:
+        raise ValueError(f"seqlens_k must have batch = {batch} elements")
+    if cu.dim() != 1 or cu.numel() != batch + 1:
+        raise ValueError(f"{cu_name} must have batch + 1 = {batch + 1} elements")
+    return batch
+
+
+def _check_like(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype) -> None:
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"(got {t.dtype} {tuple(t.shape)})")
+
+
+def _check_workspace(ws: Optional[torch.Tensor]) -> None:
+    if ws is not None and not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def _check_devices(ref: torch.Tensor, **named: Optional[torch.Tensor]) -> None:
+    """Every tensor on ref's GPU."""
+    if not ref.is_cuda:
+        raise ValueError(f"tensors must be on a GPU (got {ref.device}); the library takes device addresses")
+    for name, t in named.items():
+        if t is not None and (not t.is_cuda or t.device != ref.device):
+            raise ValueError(f"{name} is on {t.device}; every tensor must be on {ref.device}")
+
+
+def _check_new_rows(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, rows: Optional[int],
+                    what: str) -> None:
+    """k_new / v_new: contiguous [rows, Hkv, d] in the cache's dtype."""
+    hk, d = k_cache.shape[2], k_cache.shape[3]
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if (t.dim() != 3 or not t.is_contiguous() or t.dtype != k_cache.dtype or tuple(t.shape[1:]) != (hk, d)
+                or (rows is not None and t.shape[0] != rows)):
+            raise ValueError(f"{name} must be a contiguous [{what}, {hk}, {d}] tensor of the cache dtype")
+
+
 def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  block_table: torch.Tensor, seqlens_k: torch.Tensor, cu_seqlens_q: torch.Tensor,
                  causal: bool, softmax_scale: float, *, max_seqlen_q: int, max_seqlen_k: int = 0,
@@ -218,13 +274,17 @@ def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       k_scale=k_scale, v_scale=v_scale)
     if lay.head_dim != q.shape[2]:
         raise ValueError("q head_dim differs from the cache's")
+    _check_index(block_table, seqlens_k, cu_seqlens_q, "cu_seqlens_q")
+    _check_like(out, "out", q.shape, q.dtype)
+    _check_like(lse, "lse", q.shape[:2], torch.float32)
+    _check_workspace(workspace)
+    _check_devices(q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seqlens_k=seqlens_k,
+                   cu_seqlens_q=cu_seqlens_q, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
-    bt = _int32(block_table, "block_table")
-    sk = _int32(seqlens_k, "seqlens_k")
-    cu = _int32(cu_seqlens_q, "cu_seqlens_q")
+    bt, sk, cu = block_table, seqlens_k, cu_seqlens_q
     L = lib()
     args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(lay), bt.data_ptr(),
             sk.data_ptr(), cu.data_ptr(), 1 if causal else 0, float(softmax_scale), out.data_ptr(),
@@ -287,13 +347,19 @@ def attn_forward_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
     """
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [total_q, Hq, d] tensor")
-    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
-        if t.dim() != 3 or not t.is_contiguous() or t.dtype != k_cache.dtype or t.shape[0] != q.shape[0]:
-            raise ValueError(f"{name} must be a contiguous [total_q, Hkv, d] tensor of the cache dtype")
     if q.dtype != query_dtype(k_cache.dtype):
         raise TypeError("q dtype does not match the cache (bf16 queries for an FP8 cache)")
     lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k,
                       k_scale=k_scale, v_scale=v_scale)
+    if lay.head_dim != q.shape[2]:
+        raise ValueError("q head_dim differs from the cache's")
+    _check_new_rows(k_new, v_new, k_cache, q.shape[0], "total_q")
+    _check_index(block_table, seqlens_k, cu_seqlens_q, "cu_seqlens_q")
+    _check_like(out, "out", q.shape, q.dtype)
+    _check_like(lse, "lse", q.shape[:2], torch.float32)
+    _check_workspace(workspace)
+    _check_devices(q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                   seqlens_k=seqlens_k, cu_seqlens_q=cu_seqlens_q, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -320,14 +386,23 @@ def attn_chunk_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     ``part_o [max_chunks, total_q * Hq, d]`` and ``part_ml [max_chunks, total_q * Hq, 2]``
     fp32, chunk-major; allocated (uninitialised) when not given.
     """
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [total_q, Hq, d] tensor")
     if q.dtype != query_dtype(k_cache.dtype):
         raise TypeError("q dtype does not match the cache (bf16 queries for an FP8 cache)")
     lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k,
                       k_scale=k_scale, v_scale=v_scale)
+    if lay.head_dim != q.shape[2]:
+        raise ValueError("q head_dim differs from the cache's")
     if max_chunks is None:
         mk = max_seqlen_k or block_table.shape[1] * k_cache.shape[1]
         max_chunks = max(1, -(-mk // CHUNK_KEYS))
     rows = q.shape[0] * q.shape[1]
+    _check_index(block_table, seqlens_k, cu_seqlens_q, "cu_seqlens_q")
+    _check_like(part_o, "part_o", (max_chunks, rows, q.shape[2]), torch.float32)
+    _check_like(part_ml, "part_ml", (max_chunks, rows, 2), torch.float32)
+    _check_devices(q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seqlens_k=seqlens_k,
+                   cu_seqlens_q=cu_seqlens_q, part_o=part_o, part_ml=part_ml)
     if part_o is None:
         part_o = torch.empty((max_chunks, rows, q.shape[2]), dtype=torch.float32, device=q.device)
     if part_ml is None:
@@ -347,8 +422,21 @@ def attn_merge_partials(part_o: torch.Tensor, part_ml: torch.Tensor, q: torch.Te
                         v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
                         lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Fold chunk partials in ascending chunk order into ``(out, lse)`` (shapes from ``q``)."""
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, Hq, d]")
     lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k,
                       v_scale=v_scale)
+    if lay.head_dim != q.shape[2]:
+        raise ValueError("q head_dim differs from the cache's")
+    rows = q.shape[0] * q.shape[1]
+    if part_o.dim() != 3 or part_o.shape[0] < 1:
+        raise ValueError("part_o must be [max_chunks, total_q * Hq, d]")
+    _check_like(part_o, "part_o", (part_o.shape[0], rows, q.shape[2]), torch.float32)
+    _check_like(part_ml, "part_ml", (part_o.shape[0], rows, 2), torch.float32)
+    _check_index(block_table, seqlens_k, cu_seqlens_q, "cu_seqlens_q")
+    _check_like(out, "out", q.shape, q.dtype)
+    _check_like(lse, "lse", q.shape[:2], torch.float32)
+    _check_devices(part_o, part_ml=part_ml, seqlens_k=seqlens_k, cu_seqlens_q=cu_seqlens_q, out=out, lse=lse)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -382,6 +470,20 @@ def attn_backward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             raise ValueError(f"{name} must be a contiguous tensor of q's shape and dtype")
     if lse.shape != q.shape[:2] or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [total_q, Hq] tensor")
+    if q.dtype != k_cache.dtype:
+        raise TypeError("q and the cache must share the dtype (bf16 or float32)")
+    batch = _check_index(block_table, seqlens_k, cu_seqlens_q, "cu_seqlens_q")
+    if cu_seqlens_k is not None and (_int32(cu_seqlens_k, "cu_seqlens_k").dim() != 1
+                                     or cu_seqlens_k.numel() != batch + 1):
+        raise ValueError(f"cu_seqlens_k must have batch + 1 = {batch + 1} elements")
+    _check_like(dq, "dq", q.shape, q.dtype)
+    if total_k is not None:
+        for t, name in ((dk, "dk"), (dv, "dv")):
+            _check_like(t, name, (total_k, k_cache.shape[2], k_cache.shape[3]), q.dtype)
+    _check_workspace(workspace)
+    _check_devices(q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seqlens_k=seqlens_k,
+                   cu_seqlens_q=cu_seqlens_q, out=out, lse=lse, dout=dout, cu_seqlens_k=cu_seqlens_k, dq=dq,
+                   dk=dk, dv=dv, workspace=workspace)
     sk = _int32(seqlens_k, "seqlens_k")
     if cu_seqlens_k is None:
         cu_seqlens_k = torch.zeros(sk.numel() + 1, dtype=torch.int32, device=sk.device)
@@ -391,6 +493,10 @@ def attn_backward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         total_k = int(cuk[-1].item())
     lay = make_layout(k_cache, v_cache, block_table, q.shape[1], max_seqlen_q, q.shape[0], max_seqlen_k)
     hk, d = k_cache.shape[2], k_cache.shape[3]
+    if lay.head_dim != q.shape[2]:
+        raise ValueError("q head_dim differs from the cache's")
+    _check_like(dk, "dk", (total_k, hk, d), q.dtype)
+    _check_like(dv, "dv", (total_k, hk, d), q.dtype)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
@@ -430,10 +536,15 @@ def cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
     """
     if total_new is None:
         total_new = k_new.shape[0]
-    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
-        if t.dim() != 3 or not t.is_contiguous() or t.dtype != k_cache.dtype:
-            raise ValueError(f"{name} must be a contiguous [total_new, Hkv, d] tensor of the cache dtype")
     lay = make_layout(k_cache, v_cache, block_table, k_cache.shape[2], 0, 0)
+    _check_new_rows(k_new, v_new, k_cache, None, "total_new")
+    if v_new.shape[0] != k_new.shape[0]:
+        raise ValueError("k_new and v_new must have the same number of rows")
+    if not 0 <= int(total_new) <= k_new.shape[0]:
+        raise ValueError(f"total_new = {total_new} must be in [0, {k_new.shape[0]}] (the rows of k_new)")
+    _check_index(block_table, seqlens_k, cu_seqlens_new, "cu_seqlens_new")
+    _check_devices(k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                   seqlens_k=seqlens_k, cu_seqlens_new=cu_seqlens_new)
     L = lib()
     rc = L.pkv_cache_write(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                            ctypes.byref(lay), _int32(block_table, "block_table").data_ptr(),
