@@ -170,6 +170,28 @@ int pkv_attn_forward_ws(const void* q, const void* k_cache, const void* v_cache,
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * As pkv_attn_forward, allocating nothing: for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The split path's chunk partials go to a static
+ * device array of PKV_NOALLOC_MAX_BYTES bytes that the library holds on each
+ * GPU it runs on until the process ends; its address is looked up (with
+ * hipGetSymbolAddress) on the first call on each device, so make that first
+ * call outside stream capture.  No hipMalloc, hipFree or allocating library
+ * call is made.  A call whose split path needs more than PKV_NOALLOC_MAX_BYTES
+ * (pkv_attn_workspace_size) fails with PKV_ERR_WORKSPACE before any launch.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (nothing in it needs to start at zero): calls that may overlap on
+ * one GPU -- on different streams, or from different threads without
+ * ordering -- race on it and must not be issued.  Arguments, results and
+ * other errors as pkv_attn_forward; the bits equal pkv_attn_forward's.
+ */
+#define PKV_NOALLOC_MAX_BYTES ((size_t)96 << 20)
+int pkv_attn_forward_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                             const pkv_layout* kv_strides, const int32_t* block_table,
+                             const int32_t* seqlens_k, const int32_t* cu_seqlens_q, int causal,
+                             float softmax_scale, void* out, float* lse, hipStream_t stream);
+
+/*
  * Fused append-then-attend: the K/V rows of this call's own query rows are
  * written into the cache and attended in the same launch.  The step before the
  * path on the pages (aiter commit d293d61bbf19: flash_attn_with_kvcache

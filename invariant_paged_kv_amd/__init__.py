@@ -30,11 +30,13 @@ PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_ALIGN, PKV_ERR_WORKS
 PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL = 1, 2, 3
 CHUNK_KEYS = 1024
 TILE_KEYS = 64
+NOALLOC_MAX_BYTES = 96 << 20   # PKV_NOALLOC_MAX_BYTES: the static scratch of pkv_attn_forward_noalloc
 
 # Every symbol include/pkv.h declares.
 EXPORTS = (
     "pkv_attn_forward",
     "pkv_attn_forward_ws",
+    "pkv_attn_forward_noalloc",
     "pkv_attn_forward_append",
     "pkv_attn_workspace_size",
     "pkv_attn_chunk_partials",
@@ -100,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_attn_forward.restype = i32
     L.pkv_attn_forward_ws.argtypes = [vp, vp, vp, lay, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.pkv_attn_forward_ws.restype = i32
+    L.pkv_attn_forward_noalloc.argtypes = [vp, vp, vp, lay, vp, vp, vp, i32, f32, vp, vp, vp]
+    L.pkv_attn_forward_noalloc.restype = i32
     L.pkv_attn_forward_append.argtypes = [vp, vp, vp, vp, vp, lay, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.pkv_attn_forward_append.restype = i32
     L.pkv_attn_workspace_size.argtypes = [lay]
@@ -257,7 +261,7 @@ def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  causal: bool, softmax_scale: float, *, max_seqlen_q: int, max_seqlen_k: int = 0,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, k_scale: float = 1.0,
-                 v_scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
+                 v_scale: float = 1.0, noalloc: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention of packed queries ``q [total_q, Hq, d]`` against the paged cache.
 
     ``seqlens_k[b]`` keys are visible to sequence ``b`` (including its own new
@@ -289,6 +293,12 @@ def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(lay), bt.data_ptr(),
             sk.data_ptr(), cu.data_ptr(), 1 if causal else 0, float(softmax_scale), out.data_ptr(),
             lse.data_ptr())
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc uses the library's static scratch; pass no workspace")
+        rc = L.pkv_attn_forward_noalloc(*args, _stream_handle(q.device))
+        _check(rc, "pkv_attn_forward_noalloc")
+        return out, lse
     if workspace is None:
         rc = L.pkv_attn_forward(*args, _stream_handle(q.device))
     else:
@@ -296,6 +306,14 @@ def attn_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                    _stream_handle(q.device))
     _check(rc, "pkv_attn_forward")
     return out, lse
+
+
+def attn_forward_noalloc(*args, **kwargs) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``attn_forward`` through ``pkv_attn_forward_noalloc``: no device allocation
+    by the library (the split path uses its static per-GPU scratch; calls that
+    may overlap on one GPU must not be issued).  Pass ``out``/``lse`` to keep the
+    binding from allocating them."""
+    return attn_forward(*args, noalloc=True, **kwargs)
 
 
 def flash_attn_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -12,12 +12,22 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "pkv.h"
 #include "pkv_internal.h"
 
+// Device scratch of pkv_attn_forward_noalloc: the split path's chunk
+// partials (and job-order counts) for callers that cannot allocate.  Every
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code `scratch` is only a stand-in for the symbol; its device address on
+// each GPU comes from hipGetSymbolAddress and is kept per device
+// (g_scratch_ptr); only that address is ever handed to a kernel or copy.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_MAX_BYTES];
+
 namespace {
 
+constexpr size_t kScratchBytes = PKV_NOALLOC_MAX_BYTES;
 constexpr int kChunk = PKV_CHUNK_KEYS;
 static_assert(PKV_CHUNK_KEYS == 1024 && PKV_TILE_KEYS == 64, "header constants must match the device code");
 
@@ -462,6 +472,28 @@ int run_backward(const void* q, const void* k_cache, const void* v_cache, const 
   return ok();
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up once per device (with that
+// device current) on the first call that needs it.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_HIP, "no usable current device for the static scratch (device %d)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -486,6 +518,29 @@ int pkv_attn_forward_ws(const void* q, const void* k_cache, const void* v_cache,
                         hipStream_t stream) {
   return run_attention(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, causal, softmax_scale,
                        out, lse, workspace, workspace_bytes, false, stream);
+}
+
+int pkv_attn_forward_noalloc(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* kv_strides,
+                             const int32_t* block_table, const int32_t* seqlens_k, const int32_t* cu_seqlens_q,
+                             int causal, float softmax_scale, void* out, float* lse, hipStream_t stream) {
+  // every host-side check first: nothing touches the device before they pass
+  int rc = validate(kv_strides);
+  if (rc) return rc;
+  rc = check_attn_ptrs(q, k_cache, v_cache, block_table, seqlens_k, cu_seqlens_q, out, lse, *kv_strides);
+  if (rc) return rc;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(PKV_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  const size_t need = make_plan(*kv_strides).ws_bytes;
+  if (need > kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE, "the split path needs %zu scratch bytes; the static scratch holds %zu "
+                "(use pkv_attn_forward_ws with a caller workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && kv_strides->batch > 0 && kv_strides->total_q > 0) {
+    rc = scratch_ptr(&ws);
+    if (rc) return rc;
+  }
+  return run_attention(q, k_cache, v_cache, kv_strides, block_table, seqlens_k, cu_seqlens_q, causal, softmax_scale,
+                       out, lse, ws, ws ? kScratchBytes : 0, false, stream);
 }
 
 int pkv_attn_forward_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -186,3 +186,23 @@ def test_chunk_partials_and_merge_reject_bad_arguments():
     assert L.pkv_attn_merge_partials(96, 112, 0, ctypes.byref(lay), 64, 64, 1, 48, 64, None) == -2
     assert L.pkv_attn_merge_partials(None, 112, 4, ctypes.byref(lay), 64, 64, 1, 48, 64, None) == -1
     assert L.pkv_attn_merge_partials(96, 104, 4, ctypes.byref(lay), 64, 64, 1, 48, 64, None) == -4
+
+
+def test_noalloc_rejects_a_split_path_beyond_the_scratch_before_any_device_call():
+    """The size check of pkv_attn_forward_noalloc runs on the host first: on a
+    machine without a GPU it still answers PKV_ERR_WORKSPACE (a device call
+    would have failed with PKV_ERR_HIP), and nothing is launched."""
+    L = pkv.lib()
+    # 4096 decode rows x 64 heads over 2^20 keys: 4096 * 64 * 1024 chunks * 130 fp32 of partials
+    lay = good_layout(batch=1, num_heads_q=64, num_heads_k=8, block_size=256, max_blocks_per_seq=4096,
+                      total_q=4096, max_seqlen_q=1, k_block_stride=2 * 256 * 8 * 128, k_slot_stride=8 * 128,
+                      v_block_stride=2 * 256 * 8 * 128, v_slot_stride=8 * 128)
+    assert L.pkv_attn_workspace_size(ctypes.byref(lay)) > pkv.NOALLOC_MAX_BYTES
+    rc = L.pkv_attn_forward_noalloc(16, 32, 48, ctypes.byref(lay), 64, 64, 64, 1, 0.1, 80, 96, None)
+    assert rc == pkv.PKV_ERR_WORKSPACE
+    assert b"scratch" in L.pkv_last_error()
+    # a layout that fits passes the size check; a NULL q is then reported, still before any device call
+    small = good_layout()
+    assert 0 < L.pkv_attn_workspace_size(ctypes.byref(small)) <= pkv.NOALLOC_MAX_BYTES
+    assert L.pkv_attn_forward_noalloc(None, 32, 48, ctypes.byref(small), 64, 64, 64, 1, 0.1, 80, 96,
+                                      None) == pkv.PKV_ERR_NULL
