@@ -79,7 +79,8 @@ enum pkv_status {
   PKV_ERR_ALIGN = -4,     /* a pointer or stride breaks 16-byte alignment */
   PKV_ERR_WORKSPACE = -5, /* workspace too small or could not be allocated */
   PKV_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed */
-  PKV_ERR_OPTION = -7     /* unknown option or value */
+  PKV_ERR_OPTION = -7,    /* unknown option or value */
+  PKV_ERR_DEVICE_DATA = -8 /* index data violates a precondition (debug mode, pkv_check_inputs) */
 };
 
 /*
@@ -141,9 +142,12 @@ typedef struct pkv_layout {
  *   lse          device fp32 [total_q, Hq] (written): natural-log LSE
  *   stream       HIP stream; all work is enqueued there
  * Buffers must stay alive until the stream passes this call.  Device data
- * preconditions (not checked): block ids in [0, num_blocks); seqlens_k[b] <=
- * min(max_seqlen_k, max_blocks_per_seq * block_size); row counts <=
- * max_seqlen_q; cache values at visible positions finite.  A row with no
+ * preconditions (checked only in debug mode, PKV_OPT_DEBUG): cu_seqlens_q[0] = 0,
+ * non-decreasing, cu_seqlens_q[batch] = total_q; row counts <= max_seqlen_q;
+ * 0 <= seqlens_k[b] <= min(max_seqlen_k, max_blocks_per_seq * block_size);
+ * the block ids a sequence with rows uses in [0, num_blocks) (num_blocks = 0:
+ * ids only checked for >= 0).  Not checked at all: cache values at visible
+ * positions finite.  A row with no
  * visible key (e.g. seqlens_k[b] = 0, or a causal row at position < 0 when
  * seqlens_k[b] is below the row count) gets out = 0 and lse = -inf.  The split (decode)
  * path needs a workspace; this entry point takes it from the stream-ordered
@@ -305,9 +309,13 @@ size_t pkv_attn_backward_workspace_size(const pkv_layout* kv_strides);
  *                   sequence b goes to position seqlens_k[b] + t.  Not updated: the
  *                   caller advances it.
  *   cu_seqlens_new  device int32 [batch + 1]
- *   total_new       host copy of cu_seqlens_new[batch]
- * Only the written slots change.  Precondition (not checked): every target
- * position is < max_blocks_per_seq * block_size and maps to a valid block.
+ *   total_new       host copy of cu_seqlens_new[batch]: the launch has one work group
+ *                   per new token, and reading the count from cu_seqlens_new on the
+ *                   device would cost a host synchronisation per call
+ * Only the written slots change.  Preconditions (checked only in debug mode):
+ * cu_seqlens_new[0] = 0, non-decreasing, cu_seqlens_new[batch] = total_new;
+ * seqlens_k[b] >= 0; every target position < max_blocks_per_seq * block_size
+ * and its block id in [0, num_blocks).
  */
 int pkv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     const pkv_layout* kv_strides, const int32_t* block_table,
@@ -319,7 +327,9 @@ int pkv_validate_layout(const pkv_layout* kv_strides);
 
 /*
  * Process-wide tuning and test hooks.  None changes a result bit: they choose
- * which kernels run and how work is split.
+ * which kernels run and how work is split (debug mode adds checks).  They are
+ * process-wide on purpose: a setting made on one thread governs calls made on
+ * any other, and since no option changes a bit, concurrent calls stay correct.
  *   PKV_OPT_PATH          0 auto, 1 split (decode kernels + merge), 2 full (prefill kernel)
  *   PKV_OPT_SPLIT_CHUNKS  chunks handled by one split work item (0 = auto = 1, 1..64);
  *                         with one chunk per item, ragged batches spanning at most 16
@@ -328,10 +338,50 @@ int pkv_validate_layout(const pkv_layout* kv_strides);
  *                         1024 and the keys reach 16384, else 2), 1 pipelined 8 waves x
  *                         16 columns per work group, 2 4 waves x 32 columns, 3 8 waves x
  *                         32 columns (not for the fused append, which takes 2)
+ *   PKV_OPT_DEBUG         0 off, 1 debug mode: every call first enqueues a check of
+ *                         its index data (the device-data preconditions above) on its
+ *                         stream; when one fails, the call's kernels return without
+ *                         touching memory and a per-GPU error word records the
+ *                         violation, read by pkv_check_device_errors.  The word is
+ *                         sticky: until it is collected, every debug-mode call on that
+ *                         GPU does nothing.  Initially 1 when the environment variable
+ *                         PKV_DEBUG is set to a nonzero value.  The first debug-mode call
+ *                         on a device clears the word synchronously: make it outside
+ *                         stream capture.
  */
-enum pkv_option { PKV_OPT_PATH = 1, PKV_OPT_SPLIT_CHUNKS = 2, PKV_OPT_FULL_KERNEL = 3 };
+enum pkv_option { PKV_OPT_PATH = 1, PKV_OPT_SPLIT_CHUNKS = 2, PKV_OPT_FULL_KERNEL = 3, PKV_OPT_DEBUG = 4 };
 int pkv_set_option(int option, int64_t value);
 int64_t pkv_get_option(int option);
+
+/*
+ * Collect the device-side errors of the work enqueued so far (synchronises
+ * `stream`).  Returns PKV_ERR_HIP if the stream or an earlier launch failed,
+ * PKV_ERR_DEVICE_DATA (message: the violated preconditions and the lowest bad
+ * sequence) if a debug-mode check on the current device recorded a violation
+ * since the last collection -- the word is then cleared -- and PKV_OK
+ * otherwise.  Not capturable (it synchronises).
+ *   ROCm/aiter commit d293d61bbf19, commit message: a block address computed
+ *   from the wrong stride read memory outside the sequence's blocks and
+ *   "produced garbage" with no error; RL-Kernel issue #152, section Scope: the
+ *   cache write and the reads must agree on every slot.  These checks turn
+ *   such index data into an error instead of a silent wrong result.
+ */
+int pkv_check_device_errors(hipStream_t stream);
+
+/*
+ * The same precondition checks on host copies of the index data (no device
+ * call): block_table [batch, max_blocks_per_seq], seqlens_k [batch] and
+ * cu_seqlens [batch + 1], int32 host arrays, as they will be passed to
+ *   op = PKV_CHECK_ATTENTION   pkv_attn_forward* / chunk partials (total_rows = total_q)
+ *        PKV_CHECK_APPEND      pkv_attn_forward_append (also rows <= seqlens_k[b])
+ *        PKV_CHECK_CACHE_WRITE pkv_cache_write (seqlens_k before the append,
+ *                              total_rows = total_new)
+ * Returns PKV_OK or PKV_ERR_DEVICE_DATA with the violated preconditions and
+ * the first bad sequence in pkv_last_error().
+ */
+enum pkv_check_op { PKV_CHECK_ATTENTION = 0, PKV_CHECK_APPEND = 1, PKV_CHECK_CACHE_WRITE = 2 };
+int pkv_check_inputs(const pkv_layout* kv_strides, const int32_t* block_table, const int32_t* seqlens_k,
+                     const int32_t* cu_seqlens, int64_t total_rows, int op);
 
 const char* pkv_error_string(int code);
 /* Message of the calling thread's last failed call ("" if none). */

@@ -27,7 +27,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_ALIGN, PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_OPTION = \
     0, -1, -2, -3, -4, -5, -6, -7
-PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL = 1, 2, 3
+PKV_ERR_DEVICE_DATA = -8
+PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL, PKV_OPT_DEBUG = 1, 2, 3, 4
+PKV_CHECK_ATTENTION, PKV_CHECK_APPEND, PKV_CHECK_CACHE_WRITE = 0, 1, 2
 CHUNK_KEYS = 1024
 TILE_KEYS = 64
 NOALLOC_MAX_BYTES = 96 << 20   # PKV_NOALLOC_MAX_BYTES: the static scratch of pkv_attn_forward_noalloc
@@ -46,6 +48,8 @@ EXPORTS = (
     "pkv_cache_write",
     "pkv_validate_layout",
     "pkv_set_option",
+    "pkv_check_device_errors",
+    "pkv_check_inputs",
     "pkv_get_option",
     "pkv_error_string",
     "pkv_last_error",
@@ -120,6 +124,10 @@ def lib() -> ctypes.CDLL:
     L.pkv_cache_write.restype = i32
     L.pkv_validate_layout.argtypes = [lay]
     L.pkv_validate_layout.restype = i32
+    L.pkv_check_device_errors.argtypes = [vp]
+    L.pkv_check_device_errors.restype = i32
+    L.pkv_check_inputs.argtypes = [lay, vp, vp, vp, i64, i32]
+    L.pkv_check_inputs.restype = i32
     L.pkv_set_option.argtypes = [i32, i64]
     L.pkv_set_option.restype = i32
     L.pkv_get_option.argtypes = [i32]
@@ -572,6 +580,29 @@ def cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
     _check(rc, "pkv_cache_write")
 
 
+def check_device_errors(device: Optional[torch.device] = None) -> None:
+    """Synchronise the current stream and raise ``PkvError`` if a launch failed or a
+    debug-mode check (``options(debug=1)`` / ``PKV_DEBUG=1``) recorded bad index
+    data since the last call (the record is then cleared)."""
+    dev = torch.device("cuda") if device is None else device
+    _check(lib().pkv_check_device_errors(_stream_handle(dev)), "pkv_check_device_errors")
+
+
+def check_inputs(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                 seqlens_k: torch.Tensor, cu_seqlens: torch.Tensor, *, num_heads_q: int, max_seqlen_q: int,
+                 total_rows: int, op: int = PKV_CHECK_ATTENTION, max_seqlen_k: int = 0) -> None:
+    """The debug-mode precondition checks on host copies of the index data (no
+    device call); raises ``PkvError`` (``PKV_ERR_DEVICE_DATA``) naming the violations."""
+    lay = make_layout(k_cache, v_cache, block_table, num_heads_q, max_seqlen_q, total_rows, max_seqlen_k)
+    bt = block_table.detach().to("cpu", torch.int32).contiguous()
+    sk = seqlens_k.detach().to("cpu", torch.int32).contiguous()
+    cu = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    if sk.numel() != bt.shape[0] or cu.numel() != bt.shape[0] + 1:
+        raise ValueError("seqlens_k needs batch and cu_seqlens batch + 1 elements")
+    _check(lib().pkv_check_inputs(ctypes.byref(lay), bt.data_ptr(), sk.data_ptr(), cu.data_ptr(), int(total_rows),
+                                  int(op)), "pkv_check_inputs")
+
+
 def set_option(option: int, value: int) -> None:
     _check(lib().pkv_set_option(option, value), "pkv_set_option")
 
@@ -584,8 +615,10 @@ class options:
     """Context manager that sets library options and restores them on exit."""
 
     def __init__(self, path: Optional[int] = None, split_chunks: Optional[int] = None,
-                 full_kernel: Optional[int] = None):
+                 full_kernel: Optional[int] = None, debug: Optional[int] = None):
         self._want = {}
+        if debug is not None:
+            self._want[PKV_OPT_DEBUG] = debug
         if path is not None:
             self._want[PKV_OPT_PATH] = path
         if split_chunks is not None:

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["pkv_api.hip", "pkv_attn.hip", "pkv_attn_bwd.hip", "pkv_cache_write.hip"]
+SOURCES = ["pkv_api.hip", "pkv_attn.hip", "pkv_attn_bwd.hip", "pkv_cache_write.hip", "pkv_debug.hip"]
 
 # -ffp-contract=off: no implicit FMA contraction, so the same source gives the
 # same instruction-level arithmetic in every kernel that calls it.  The

@@ -11,10 +11,12 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
 #include "pkv.h"
+#include "pkv_checks.h"
 #include "pkv_internal.h"
 
 // Device scratch of pkv_attn_forward_noalloc: the split path's chunk
@@ -24,6 +26,11 @@
 // each GPU comes from hipGetSymbolAddress and is kept per device
 // (g_scratch_ptr); only that address is ever handed to a kernel or copy.
 static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_MAX_BYTES];
+
+// Debug mode's error word on each GPU: [0] violation flags (pkv_checks.h),
+// [1] 0x7fffffff minus the lowest bad sequence (0: none).  Sticky until
+// pkv_check_device_errors reads and clears it.
+static __device__ __align__(256) int32_t dbg_word[4];
 
 namespace {
 
@@ -35,6 +42,15 @@ thread_local char g_msg[512] = "";
 std::atomic<int64_t> g_opt_path{0};
 std::atomic<int64_t> g_opt_split_chunks{0};
 std::atomic<int64_t> g_opt_full_kernel{0};
+// Debug mode: PKV_OPT_DEBUG, initially on when the environment sets PKV_DEBUG to a nonzero value.
+int64_t env_debug() {
+  const char* e = std::getenv("PKV_DEBUG");
+  return (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+}
+std::atomic<int64_t> g_opt_debug{env_debug()};
+#ifndef PKV_PART_CHUNK_MAJOR
+#define PKV_PART_CHUNK_MAJOR 0
+#endif
 #ifndef PKV_DECODE_LPT
 #define PKV_DECODE_LPT 1
 #endif
@@ -50,6 +66,81 @@ int fail(int code, const char* fmt, ...) {
 int ok() {
   g_msg[0] = '\0';
   return PKV_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up once per device (with that
+// device current) on the first call that needs it.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_HIP, "no usable current device for the static scratch (device %d)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+// The current device's debug error word, looked up (and cleared) once per
+// device; debug mode only.
+int32_t* g_dbg_ptr[kMaxDevices] = {};
+
+int dbg_word_ptr(int32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_HIP, "no usable current device for the debug error word (device %d)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_dbg_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(dbg_word));
+    const int32_t zero[4] = {0, 0, 0, 0};
+    if (e == hipSuccess && p) e = hipMemcpy(p, zero, sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess || !p)
+      return fail(PKV_ERR_HIP, "debug error word on device %d: %s", dev, hipGetErrorString(e));
+    g_dbg_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_dbg_ptr[dev];
+  return PKV_OK;
+}
+
+// Debug mode (PKV_OPT_DEBUG): enqueue the check kernel of the call's index
+// data ahead of its kernels and hand them the error word; otherwise nothing
+// (*word = NULL: the kernels skip no work).
+int debug_check(const pkv::CheckLimits& lim, const int32_t* cu, const int32_t* sk, const int32_t* bt,
+                const int32_t* cu_k, hipStream_t stream, const int32_t** word) {
+  *word = nullptr;
+  if (!g_opt_debug.load()) return PKV_OK;
+  int32_t* w = nullptr;
+  int rc = dbg_word_ptr(&w);
+  if (rc) return rc;
+  const hipError_t e = pkv::launch_check(lim, cu, sk, bt, cu_k, w, stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "debug check launch failed: %s", hipGetErrorString(e));
+  *word = w;
+  return PKV_OK;
+}
+
+int64_t max_seqlen_k_of(const pkv_layout& l);
+
+pkv::CheckLimits check_limits(const pkv_layout& l, int op, int64_t total_rows) {
+  pkv::CheckLimits c{};
+  c.total_rows = total_rows;
+  c.max_k = op == pkv::kOpCacheWrite ? static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size : max_seqlen_k_of(l);
+  c.num_blocks = l.num_blocks;
+  c.max_rows = l.max_seqlen_q;
+  c.mbps = l.max_blocks_per_seq;
+  c.bs = l.block_size;
+  c.batch = l.batch;
+  c.op = op;
+  return c;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -271,8 +362,8 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.cpi = p.cpi;
   a.chunk0 = 0;
   a.chunk1 = p.maxc;
-  a.ps_row = p.maxc;
-  a.ps_chunk = 1;
+  a.ps_row = PKV_PART_CHUNK_MAJOR ? 1 : p.maxc;
+  a.ps_chunk = PKV_PART_CHUNK_MAJOR ? l->total_q * l->num_heads_q : 1;
   a.causal = causal ? 1 : 0;
   a.mul = score_mul(*l, softmax_scale);
   a.v_scale = kv_scale(l->v_scale);
@@ -284,6 +375,12 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.job_pref = p.lp.lpt ? reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + p.off_jobs) : nullptr;
   a.nbatch = l->batch;
   a.nhk = l->num_heads_k;
+  rc = debug_check(check_limits(*l, append ? pkv::kOpAppend : pkv::kOpAttention, l->total_q), cu_seqlens_q,
+                   seqlens_k, block_table, nullptr, stream, &a.dbg_word);
+  if (rc) {
+    if (allocated) (void)hipFreeAsync(ws, stream);
+    return rc;
+  }
   hipError_t e = pkv::launch_attention(a, p.lp, l->dtype, l->head_dim, stream);
   if (allocated) {
     hipError_t fe = hipFreeAsync(ws, stream);
@@ -354,6 +451,9 @@ int run_partials(const void* q, const void* k_cache, const void* v_cache, const 
   a.mul = score_mul(*l, softmax_scale);
   a.v_scale = kv_scale(l->v_scale);
   pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
+  rc = debug_check(check_limits(*l, pkv::kOpAttention, l->total_q), cu_seqlens_q, seqlens_k, block_table, nullptr,
+                   stream, &a.dbg_word);
+  if (rc) return rc;
   hipError_t e = pkv::launch_attention(a, lp, l->dtype, l->head_dim, stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "partials launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -384,6 +484,9 @@ int run_merge(const float* part_o, const float* part_ml, int32_t max_chunks, con
   m.v_scale = kv_scale(l->v_scale);
   m.ps_row = 1;
   m.ps_chunk = l->total_q * l->num_heads_q;
+  rc = debug_check(check_limits(*l, pkv::kOpAttention, l->total_q), cu_seqlens_q, seqlens_k, nullptr, nullptr, stream,
+                   &m.dbg_word);
+  if (rc) return rc;
   hipError_t e = pkv::launch_merge(m, l->dtype, l->head_dim, stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -463,6 +566,13 @@ int run_backward(const void* q, const void* k_cache, const void* v_cache, const 
   b.scale = softmax_scale;
   b.nkb = total_k > 0 ? static_cast<int>((mk + 16 * kWaves - 1) / (16 * kWaves)) : 0;
   pkv::BwdPlan pl{l->batch, l->num_heads_k, l->total_q, cols, mk};
+  pkv::CheckLimits lim = check_limits(*l, pkv::kOpBackward, l->total_q);
+  lim.total_k = total_k;
+  rc = debug_check(lim, cu_seqlens_q, seqlens_k, block_table, cu_seqlens_k, stream, &a.dbg_word);
+  if (rc) {
+    if (allocated) (void)hipFreeAsync(ws, stream);
+    return rc;
+  }
   hipError_t e = pkv::launch_backward(b, pl, l->dtype, l->head_dim, stream);
   if (allocated) {
     hipError_t fe = hipFreeAsync(ws, stream);
@@ -472,27 +582,6 @@ int run_backward(const void* q, const void* k_cache, const void* v_cache, const 
   return ok();
 }
 
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch_ptr[kMaxDevices] = {};
-
-// The current device's scratch address, looked up once per device (with that
-// device current) on the first call that needs it.
-int scratch_ptr(void** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return fail(PKV_ERR_HIP, "no usable current device for the static scratch (device %d)", dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_ptr[dev]) {
-    void* p = nullptr;
-    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess || !p)
-      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
-    g_scratch_ptr[dev] = p;
-  }
-  *out = g_scratch_ptr[dev];
-  return PKV_OK;
-}
 
 }  // namespace
 
@@ -613,9 +702,66 @@ int pkv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v
   a.mbps = l->max_blocks_per_seq;
   a.row_bytes = l->head_dim * elem_bytes(l->dtype);
   pkv::block_size_divisor(l->block_size, &a.bs_mul, &a.bs_shift);
+  rc = debug_check(check_limits(*l, pkv::kOpCacheWrite, total_new), cu_seqlens_new, seqlens_k, block_table, nullptr,
+                   stream, &a.dbg_word);
+  if (rc) return rc;
   hipError_t e = pkv::launch_cache_write(a, elem_bytes(l->dtype), total_new, stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "cache_write launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int pkv_check_device_errors(hipStream_t stream) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "stream synchronisation failed: %s", hipGetErrorString(e));
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pending HIP error: %s", hipGetErrorString(e));
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ok();
+  int32_t* w = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    w = g_dbg_ptr[dev];
+  }
+  if (!w) return ok();  // debug mode never ran on this device
+  int32_t h[4] = {0, 0, 0, 0};
+  e = hipMemcpy(h, w, sizeof h, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "reading the debug error word failed: %s", hipGetErrorString(e));
+  if (h[0] == 0) return ok();
+  const int32_t zero[4] = {0, 0, 0, 0};
+  e = hipMemcpy(w, zero, sizeof zero, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "clearing the debug error word failed: %s", hipGetErrorString(e));
+  return fail(PKV_ERR_DEVICE_DATA, "device data violates preconditions (flags 0x%x:%s%s%s%s%s%s%s), first at sequence %d",
+              h[0], (h[0] & pkv::kBadCu) ? " cu_seqlens" : "", (h[0] & pkv::kBadSeqlen) ? " seqlens_k" : "",
+              (h[0] & pkv::kBadBlockId) ? " block_id" : "", (h[0] & pkv::kBadRows) ? " rows>max_seqlen_q" : "",
+              (h[0] & pkv::kBadAppend) ? " append_rows>keys" : "", (h[0] & pkv::kBadWritePos) ? " write_position" : "",
+              (h[0] & pkv::kBadCuK) ? " cu_seqlens_k" : "", 0x7fffffff - h[1]);
+}
+
+int pkv_check_inputs(const pkv_layout* kv_strides, const int32_t* block_table, const int32_t* seqlens_k,
+                     const int32_t* cu_seqlens, int64_t total_rows, int op) {
+  int rc = validate(kv_strides);
+  if (rc) return rc;
+  if (op != PKV_CHECK_ATTENTION && op != PKV_CHECK_APPEND && op != PKV_CHECK_CACHE_WRITE)
+    return fail(PKV_ERR_OPTION, "op %d is not PKV_CHECK_ATTENTION, PKV_CHECK_APPEND or PKV_CHECK_CACHE_WRITE", op);
+  if (total_rows < 0) return fail(PKV_ERR_SHAPE, "total_rows %lld < 0", (long long)total_rows);
+  if (kv_strides->batch == 0) return ok();
+  if (!seqlens_k || !cu_seqlens || (kv_strides->max_blocks_per_seq > 0 && !block_table))
+    return fail(PKV_ERR_NULL, "block_table, seqlens_k or cu_seqlens is NULL");
+  const int cop = op == PKV_CHECK_ATTENTION ? pkv::kOpAttention : op == PKV_CHECK_APPEND ? pkv::kOpAppend : pkv::kOpCacheWrite;
+  const pkv::CheckLimits lim = check_limits(*kv_strides, cop, total_rows);
+  int32_t flags = 0;
+  int first = -1;
+  for (int b = 0; b < kv_strides->batch; ++b) {
+    const int32_t f = pkv::check_sequence(lim, b, cu_seqlens, seqlens_k, block_table, nullptr);
+    if (f && first < 0) first = b;
+    flags |= f;
+  }
+  if (!flags) return ok();
+  return fail(PKV_ERR_DEVICE_DATA, "index data violates preconditions (flags 0x%x:%s%s%s%s%s%s), first at sequence %d",
+              flags, (flags & pkv::kBadCu) ? " cu_seqlens" : "", (flags & pkv::kBadSeqlen) ? " seqlens_k" : "",
+              (flags & pkv::kBadBlockId) ? " block_id" : "", (flags & pkv::kBadRows) ? " rows>max_seqlen_q" : "",
+              (flags & pkv::kBadAppend) ? " append_rows>keys" : "", (flags & pkv::kBadWritePos) ? " write_position" : "",
+              first);
 }
 
 int pkv_set_option(int option, int64_t value) {
@@ -632,6 +778,10 @@ int pkv_set_option(int option, int64_t value) {
       if (value < 0 || value > 3) return fail(PKV_ERR_OPTION, "PKV_OPT_FULL_KERNEL must be in 0..3");
       g_opt_full_kernel.store(value);
       return ok();
+    case PKV_OPT_DEBUG:
+      if (value < 0 || value > 1) return fail(PKV_ERR_OPTION, "PKV_OPT_DEBUG must be 0 or 1");
+      g_opt_debug.store(value);
+      return ok();
     default:
       return fail(PKV_ERR_OPTION, "unknown option %d", option);
   }
@@ -642,6 +792,7 @@ int64_t pkv_get_option(int option) {
     case PKV_OPT_PATH: return g_opt_path.load();
     case PKV_OPT_SPLIT_CHUNKS: return g_opt_split_chunks.load();
     case PKV_OPT_FULL_KERNEL: return g_opt_full_kernel.load();
+    case PKV_OPT_DEBUG: return g_opt_debug.load();
     default: return -1;
   }
 }
@@ -656,6 +807,7 @@ const char* pkv_error_string(int code) {
     case PKV_ERR_WORKSPACE: return "workspace too small or unavailable";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_OPTION: return "invalid option";
+    case PKV_ERR_DEVICE_DATA: return "device data violates a precondition";
     default: return "unknown error";
   }
 }

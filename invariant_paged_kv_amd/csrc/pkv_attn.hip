@@ -72,6 +72,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND, bool U>
 __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a) {
+  if (dbg_skip(a.dbg_word)) return;
   using G_ = TileGeom<T, D>;
   constexpr int COLS = W * NT * 16;
   // bf16/FP8 with 4 waves: the next tile's loads are issued between the
@@ -651,6 +652,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, const int32_t* b
 
 template <class T, int D, int W, bool APPEND>
 __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
+  if (dbg_skip(a.dbg_word)) return;
   using G_ = TileGeom<T, D>;
   constexpr int COLS = W * 16;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * G_::BYTES];  // 2 x (K, V)
@@ -735,6 +737,7 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
 // (32 KiB at d = 128) of K/V loads in flight while it computes the previous one.
 template <class T, int D, bool APPEND, bool U>
 __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
+  if (dbg_skip(a.dbg_word)) return;
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
 
@@ -884,6 +887,7 @@ __device__ __forceinline__ void decode2_tile(const AttnArgs& a, const int32_t* b
 
 template <class T, int D, bool APPEND, bool U>
 __global__ __launch_bounds__(64, T::KVB == 1 ? 2 : 1) void decode2_kernel(AttnArgs a) {
+  if (dbg_skip(a.dbg_word)) return;
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
 
@@ -1003,6 +1007,7 @@ __device__ __forceinline__ void merge_fold(int c0, int nck, const float (&mc)[PF
 // so a wave waits for one round's latency at a time, not for every round.
 template <class T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  if (dbg_skip(a.dbg_word)) return;
   constexpr int WPR = kMergeWavesPerRow;
   constexpr int EPL = D / 64 / WPR > 0 ? D / 64 / WPR : 1;
   constexpr int PF = PKV_MERGE_PF;
@@ -1135,6 +1140,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
   m.ps_chunk = a.ps_chunk;
   m.causal = a.causal;
   m.v_scale = a.v_scale;
+  m.dbg_word = a.dbg_word;
   const int64_t waves = pl.total_q * a.hq;
   if (waves == 0) return hipSuccess;
   dim3 mgrid(static_cast<unsigned>((waves * kMergeWavesPerRow + 3) / 4));

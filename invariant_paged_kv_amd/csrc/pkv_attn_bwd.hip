@@ -85,6 +85,7 @@ __device__ __forceinline__ void xcd_order(int& x, int& y, int& z) {
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t pairs) {
+  if (dbg_skip(a.f.dbg_word)) return;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   constexpr int EPL = D / 16;
@@ -179,6 +180,7 @@ __device__ __forceinline__ void row_operands_global(const void* base, int64_t ro
 // ---------------------------------------------------------------------------
 template <class T, int D, int W, int NT, bool U>
 __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdArgs ba) {
+  if (dbg_skip(ba.f.dbg_word)) return;
   const AttnArgs& a = ba.f;
   using G_ = TileGeom<T, D>;
   constexpr int COLS = 16 * W * NT;
@@ -389,6 +391,7 @@ __device__ __forceinline__ void col_stage_store(unsigned char* buf, const ColSta
 // every Q / dO operand read from LDS serves all of them.
 template <class T, int D, int W, int KW>
 __global__ __launch_bounds__(64 * W, (T::EB == 2 && KW == 1) ? 3 : 2) void bwd_dkdv_kernel(BwdArgs ba) {
+  if (dbg_skip(ba.f.dbg_word)) return;
   const AttnArgs& a = ba.f;
   using C_ = ColTile<T, D>;
   constexpr int NK = C_::NK;

@@ -18,6 +18,7 @@ typedef uint32_t u32x4_cw __attribute__((ext_vector_type(4)));
 // token's position is looked up (its source does not depend on it), so the
 // lookup's loads and the row's load are in flight together.
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int eb) {
+  if (dbg_skip(a.dbg_word)) return;
   const int64_t tok = blockIdx.x;
   const int cpr = a.row_bytes / 16;
   const int per_tensor = a.hk * cpr;

@@ -50,6 +50,9 @@ struct AttnArgs {
   const int32_t* job_pref;
   int32_t nbatch;
   int32_t nhk;
+  // Debug mode: the device error word the call's check kernel wrote; every
+  // kernel of the call returns at once when it is nonzero.  NULL otherwise.
+  const int32_t* dbg_word;
 };
 
 struct MergeArgs {
@@ -63,6 +66,7 @@ struct MergeArgs {
   int32_t batch, hq, maxc, causal;
   float v_scale;
   int64_t ps_row, ps_chunk;  // partial layout, as in AttnArgs
+  const int32_t* dbg_word;   // as in AttnArgs
 };
 
 // Column groups of 16 per wave in the 4-wave split kernel (more than 16
@@ -98,7 +102,14 @@ struct CacheWriteArgs {
   int32_t batch, hk, bs, mbps, row_bytes;
   uint32_t bs_mul;
   int32_t bs_shift;
+  const int32_t* dbg_word;  // as in AttnArgs
 };
+
+// True when debug mode found bad device data for this call (or an earlier
+// one not yet collected by pkv_check_device_errors): the kernel does nothing.
+__device__ __forceinline__ bool dbg_skip(const int32_t* w) {
+  return w != nullptr && *w != 0;
+}
 
 // Division by the block size as a multiply and shift: with l = ceil(log2 bs),
 // s = 30 + l and m = ceil(2^s / bs), floor(j / bs) == (j * m) >> s for every
@@ -161,6 +172,12 @@ struct BwdPlan {
 };
 
 hipError_t launch_attention(const AttnArgs& a, const LaunchPlan& pl, int dtype, int d, hipStream_t stream);
+// Debug mode: one thread per sequence checks the call's index data
+// (pkv_checks.h) and ORs its flags into word[0], the lowest bad sequence into
+// word[1] (atomic min).
+struct CheckLimits;
+hipError_t launch_check(const CheckLimits& l, const int32_t* cu, const int32_t* sk, const int32_t* block_table,
+                        const int32_t* cu_k, int32_t* word, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, const BwdPlan& pl, int dtype, int d, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& m, int dtype, int d, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, int elem_bytes, int64_t total_new, hipStream_t stream);
