@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--seqlen-k", type=int, default=131072)
     return ap.parse_args()
@@ -185,7 +186,24 @@ def main():
                               "kv_GBs": round(kv_bytes / (fused_ms * 1e-3) / 1e9, 2),
                               "bitwise_eq_unfused": fused_same},
     }
-    del ws, p_out, p_lse
+    del p_out, p_lse
+
+    # the default entry point, which takes the workspace from the stream-ordered
+    # allocator inside every call (pkv_attn_forward without a workspace)
+    def default_call():
+        pkv.attn_forward(q, pool.k, pool.v, bt, seqlens, cu, True, scale, max_seqlen_q=1, max_seqlen_k=N,
+                         out=out_f, lse=lse_f)
+
+    settle(torch, default_call, min_ms=50.0)
+    d_times = event_times(torch, default_call, args.steps)
+    ws_times = event_times(torch, lambda: pkv.attn_forward(q, pool.k, pool.v, bt, seqlens, cu, True, scale,
+                                                           max_seqlen_q=1, max_seqlen_k=N, out=out_f, lse=lse_f,
+                                                           workspace=ws), args.steps)
+    result["default_entry_point"] = {
+        "api": "pkv_attn_forward (workspace from hipMallocAsync/hipFreeAsync inside the call)",
+        "ms_median": round(d_times[len(d_times) // 2], 4),
+        "ws_api_ms_median": round(ws_times[len(ws_times) // 2], 4)}
+    del ws
 
     # The re-score of the generate-then-rescore workload: a 64-row causal
     # prefill per sequence over the same 131072-key cache (full path).
@@ -212,6 +230,8 @@ def main():
                                  "flops": rs_flops}
     del q_rs
 
+    if not args.no_configs:
+        result["decode_configs"] = bench_decode_configs(torch, pkv, gen, want_cpu=not args.no_cpu_baseline)
     if not args.no_fp8:
         result["fp8_decode"] = bench_fp8_decode(torch, pkv, gen, B, N, args.steps, args.warmup, attn_avg_ms)
     if not args.no_prefill:
@@ -221,6 +241,183 @@ def main():
         result["cpu_baseline"], result["oracle_parity"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale,
                                                                        out, lse)
     print(json.dumps(result), flush=True)
+
+
+FLUSH_BYTES = 1 << 30   # > L2 (8 x 4 MB) + the 256 MB Infinity Cache
+
+
+def event_times(torch, fn, reps: int, flush=None):
+    """Per-call HIP-event times (ms) of fn on the current stream: cold (a 1 GiB
+    read before each call evicts L2 and the Infinity Cache) when `flush` is
+    given, else warm (calls back to back, one event pair around each).  The
+    flush reads rather than writes: a written flush leaves the caches full of
+    dirty lines whose write-back then lands inside the timed call."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        if flush is not None:
+            flush.view(torch.int32).max()
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in evs)
+
+
+def decode_workloads():
+    """The decode workloads other than the long-context one, with their recipes."""
+    return [
+        dict(name="single sequence fp32 (339 cached + 1 appended, decode over 340 keys)", key="fp32_single",
+             dtype="f32", batch=1, hq=2, hk=2, d=64, bs=16, layout="contiguous", causal=False, seed=1001,
+             lens=lambda g: [340], rows=lambda g: [1]),
+        dict(name="decode, Qwen3-8B-like shard: batch 64 x 4096 keys, Hq 16 / Hkv 4", key="qwen_shard",
+             dtype="bf16", batch=64, hq=16, hk=4, d=128, bs=16, layout="interleaved", causal=True, seed=1002,
+             lens=lambda g: [4096] * 64, rows=lambda g: [1] * 64),
+        dict(name="ragged / padded decode: batch 128, keys U{1..8192}, 3-row slots, Hq 32 / Hkv 8",
+             key="ragged_padded", dtype="bf16", batch=128, hq=32, hk=8, d=128, bs=256, layout="interleaved",
+             causal=True, seed=1003, lens=lambda g: g.uniform_int(1, 8192, 128, generator=torch_gen(1003)),
+             rows=lambda g: [3] * 128),
+    ]
+
+
+def torch_gen(seed):
+    import torch
+    return torch.Generator().manual_seed(seed)
+
+
+def bench_decode_configs(torch, pkv, gen, reps: int = 30, want_cpu: bool = True):
+    """Cold and warm per-call timings of the other decode workloads, each with its
+    roofline (K/V bytes of the visible keys + q/out/lse/table, against 8 TB/s),
+    bitwise decode == prefill, and the oracle's agreement and host throughput on
+    a bounded sample of the same call."""
+    dev = "cuda"
+    flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    results = []
+    for w in decode_workloads():
+        B, HQ, HK, D, BS = w["batch"], w["hq"], w["hk"], w["d"], w["bs"]
+        lens = [int(x) for x in w["lens"](gen)]
+        rows = w["rows"](gen)
+        mk = max(lens)
+        nb = gen.pool_num_blocks(mk, BS, B)
+        g = torch.Generator(device=dev).manual_seed(w["seed"])
+        pool = gen.new_pool(nb, BS, HK, D, w["dtype"], w["layout"], device=dev, generator=g)
+        bt = gen.randperm_block_table(nb, B, generator=torch.Generator().manual_seed(w["seed"])).to(dev)
+        cu_l = [0]
+        for r in rows:
+            cu_l.append(cu_l[-1] + r)
+        q = gen.randn((cu_l[-1], HQ, D), w["dtype"], generator=g, device=dev)
+        sk = torch.tensor(lens, dtype=torch.int32, device=dev)
+        cu = torch.tensor(cu_l, dtype=torch.int32, device=dev)
+        scale = 1.0 / math.sqrt(D)
+        out = torch.empty_like(q)
+        lse = torch.empty((q.shape[0], HQ), dtype=torch.float32, device=dev)
+        Lq = max(rows)
+        ws = torch.empty(max(256, pkv.workspace_size(q, pool.k, pool.v, bt, max_seqlen_q=Lq, max_seqlen_k=mk)),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu, w["causal"], scale, max_seqlen_q=Lq, max_seqlen_k=mk,
+                             out=out, lse=lse, workspace=ws)
+
+        settle(torch, call, min_ms=100.0)
+        cold = event_times(torch, call, reps, flush)
+        warm = event_times(torch, call, reps)
+        eb = 4 if w["dtype"] == "f32" else 2
+        kv = sum(lens) * HK * D * eb * 2
+        nbytes = kv + 2 * q.numel() * eb + lse.numel() * 4 + sum(math.ceil(n / BS) for n in lens) * 4 + (2 * B + 1) * 4
+        med_c, med_w = cold[len(cold) // 2], warm[len(warm) // 2]
+        with pkv.options(path=2):
+            p_out, p_lse = pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu, w["causal"], scale, max_seqlen_q=Lq,
+                                            max_seqlen_k=mk)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(p_out.contiguous().view(torch.int32 if eb == 4 else torch.int16),
+                                out.view(torch.int32 if eb == 4 else torch.int16))
+                    and torch.equal(p_lse.view(torch.int32), lse.view(torch.int32)))
+        gbs = nbytes / (med_c * 1e-3) / 1e9
+        res = {"workload": w["name"], "dtype": w["dtype"], "batch": B, "num_heads_q": HQ, "num_heads_k": HK,
+               "head_dim": D, "block_size": BS, "layout": w["layout"], "keys_total": sum(lens),
+               "rows": cu_l[-1], "bytes_per_launch": nbytes,
+               "cold_ms_median": round(med_c, 4), "cold_ms_min": round(cold[0], 4),
+               "warm_ms_median": round(med_w, 4), "warm_ms_min": round(warm[0], 4),
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "timing": "cold (1 GiB flush before each call)"},
+               "warm_GBs": round(nbytes / (med_w * 1e-3) / 1e9, 2),
+               "tokens_per_s": round(cu_l[-1] / (med_c * 1e-3), 1),
+               "bitwise_decode_eq_prefill_kernel": same}
+        if want_cpu:
+            res["oracle"] = oracle_sample(torch, pool, bt, q, lens, cu_l, w, out, lse, scale,
+                                          budget_s=3.0 if B > 1 else 1.0, one_thread=w["key"] != "ragged_padded")
+        results.append(res)
+        del pool, ws, out, lse, p_out, p_lse, q
+        torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
+    return results
+
+
+def oracle_sample(torch, pool, bt, q, lens, cu_l, w, out, lse, scale, budget_s: float, one_thread: bool):
+    """The float64 oracle on whole sequences of the call, until `budget_s` of host
+    time is spent (all host threads; also on one thread for the small workloads):
+    K/V bytes per second of host time and the max-abs agreement with the GPU."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+
+    HQ, HK, D, BS = w["hq"], w["hk"], w["d"], w["bs"]
+    eb = 4 if w["dtype"] == "f32" else 2
+    gout = out.double().cpu().numpy()
+    glse = lse.double().cpu().numpy()
+
+    def host_seq(b):
+        n = lens[b]
+        nblk = math.ceil(n / BS)
+        ids = bt[b, :nblk].long()
+        kh = pool.k.index_select(0, ids).cpu().contiguous()
+        vh = pool.v.index_select(0, ids).cpu().contiguous()
+        cast = (lambda t: t.numpy().reshape(-1)) if eb == 4 else \
+            (lambda t: t.view(torch.int16).numpy().view(np.uint16).reshape(-1))
+        row = HK * D
+        lay = oracle.Layout(w["dtype"], HQ, HK, D, BS, 0, (BS * row, row, D), 0, (BS * row, row, D))
+        r0, r1 = cu_l[b], cu_l[b + 1]
+        qh = q[r0:r1].cpu()
+        qh = qh.numpy() if eb == 4 else qh.view(torch.int16).numpy().view(np.uint16)
+        return n, nblk, cast(kh), cast(vh), lay, qh, r0, r1
+
+    def run(threads):
+        done, spent, seqs, eo, el = 0, 0.0, 0, 0.0, 0.0
+        order = sorted(range(len(lens)), key=lambda b: lens[b])   # short sequences first: more of them fit
+        for b in order:
+            n, nblk, kf, vf, lay, qh, r0, r1 = host_seq(b)
+            t0 = time.perf_counter()
+            if threads is None:
+                oo, ol = oracle.attention(qh, kf, vf, lay, np.arange(nblk, dtype=np.int32)[None, :], [n],
+                                          [0, r1 - r0], w["causal"], scale)
+            else:
+                with threadpool_limits(threads):
+                    oo, ol = oracle.attention(qh, kf, vf, lay, np.arange(nblk, dtype=np.int32)[None, :], [n],
+                                              [0, r1 - r0], w["causal"], scale)
+            spent += time.perf_counter() - t0
+            fin = np.isfinite(ol)
+            eo = max(eo, float(np.max(np.abs(gout[r0:r1] - oo))))
+            el = max(el, float(np.max(np.abs(glse[r0:r1][fin] - ol[fin]))) if fin.any() else 0.0)
+            seqs += 1
+            done += n * HK * D * eb * 2
+            if spent >= budget_s:
+                break
+        return done, spent, seqs, eo, el
+
+    done, spent, seqs, eo, el = run(None)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    res = {"value": round(done / spent / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{seqs} of {len(lens)} sequences ({spent:.2f} s)",
+           "out_max_abs": eo, "lse_max_abs": el}
+    if one_thread:
+        d1, s1, n1, _, _ = run(1)
+        res["one_thread"] = {"value": round(d1 / s1 / 1e9, 5), "unit": "GB/s", "cores": 1,
+                             "sample": f"{n1} of {len(lens)} sequences ({s1:.2f} s)"}
+    return res
 
 
 def measured_traffic():

@@ -48,9 +48,6 @@ int64_t env_debug() {
   return (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
 }
 std::atomic<int64_t> g_opt_debug{env_debug()};
-#ifndef PKV_PART_CHUNK_MAJOR
-#define PKV_PART_CHUNK_MAJOR 0
-#endif
 #ifndef PKV_DECODE_LPT
 #define PKV_DECODE_LPT 1
 #endif
@@ -362,8 +359,8 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.cpi = p.cpi;
   a.chunk0 = 0;
   a.chunk1 = p.maxc;
-  a.ps_row = PKV_PART_CHUNK_MAJOR ? 1 : p.maxc;
-  a.ps_chunk = PKV_PART_CHUNK_MAJOR ? l->total_q * l->num_heads_q : 1;
+  a.ps_row = p.maxc;
+  a.ps_chunk = 1;
   a.causal = causal ? 1 : 0;
   a.mul = score_mul(*l, softmax_scale);
   a.v_scale = kv_scale(l->v_scale);

@@ -66,6 +66,15 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #ifndef PKV_FULL_DB
 #define PKV_FULL_DB 1
 #endif
+#ifndef PKV_SKIP_DEAD_WAVES
+#define PKV_SKIP_DEAD_WAVES 1
+#endif
+#ifndef PKV_SPLIT_W
+#define PKV_SPLIT_W 8
+#endif
+#ifndef PKV_IDS_AHEAD
+#define PKV_IDS_AHEAD 1
+#endif
 #ifndef PKV_SPLIT_LATE_COMMIT
 #define PKV_SPLIT_LATE_COMMIT 1
 #endif
@@ -84,7 +93,8 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
   // fused-append variant (whose store of the new rows would spill) load each
   // tile when it starts.  Past the item's last tile the rows clamp to
   // jmax - 1, so the extra loads stay in bounds.
-  constexpr bool kPrefetch = PKV_FULL_PREFETCH && T::EB == 2 && (W == 4 || W == 8) && !APPEND;
+  // (the 8-wave split kernel has the registers for it with fused append too)
+  constexpr bool kPrefetch = PKV_FULL_PREFETCH && T::EB == 2 && (W == 4 || W == 8) && (!APPEND || (SPLIT && W == 8));
   constexpr bool kDouble = kPrefetch && PKV_FULL_DB;
   // Split kernel (no running fold state, so registers to spare): the staged
   // tile t+1 is written into the idle LDS buffer between the softmax and the
@@ -93,6 +103,7 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
   // second half of one.  The buffer is free there: every wave passed the
   // barrier that ended tile t-1, its last reader.
   constexpr bool kLateCommit = kDouble && SPLIT && PKV_SPLIT_LATE_COMMIT;
+  constexpr bool kSkipDead = SPLIT && PKV_SKIP_DEAD_WAVES != 0;
   __shared__ __attribute__((aligned(16))) unsigned char lds[(kDouble ? 2 : 1) * G_::BYTES];
   unsigned char* k_lds = lds;
   unsigned char* v_lds = lds + G_::KBYTES;
@@ -160,6 +171,10 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
     }
   }
 
+  // A wave none of whose columns exists (the last column block of a
+  // sequence) skips the arithmetic; its lanes still load their share of every
+  // tile.  Wave-uniform, so barriers and loads stay the same for all waves.
+  const bool live = __builtin_amdgcn_readfirstlane(col0 + wave * NT * 16 < ncols ? 1 : 0) != 0;
   float M[NT], Ls[NT];
   f32x4 O[NT][D / 16];
   if constexpr (!SPLIT) {
@@ -177,62 +192,83 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
   // nothing is loaded and the columns get out = 0, lse = -inf.
   if (c_begin < c_end) {
     TileStage<T, D, W> stg;
-    if constexpr (kPrefetch) tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC, jmax, stg, ap);
+    // block ids of the next tile to issue, fetched one tile ahead (U)
+    TileIds ids;
+    // (split kernel only: 20.55 against 21.13 ms on the 17-token chunked
+    // prefill; the full path, with two work groups per CU hiding the id
+    // loads, measured 1.7% slower with it)
+    constexpr bool kIds = kPrefetch && U && SPLIT && PKV_IDS_AHEAD;
+    const int jb = c_begin * KC;
+    auto issue = [&](int j, TileStage<T, D, W>& into) {
+      tile_issue<T, D, W, APPEND, U, kIds>(a, bt, hk, j, jmax, into, ap, ids);
+      if constexpr (kIds) tile_ids_fetch<T, D, W, U>(a, bt, j + KT, jmax, ids);
+    };
+    if constexpr (kIds) tile_ids_fetch<T, D, W, U>(a, bt, jb, jmax, ids);
+    if constexpr (kPrefetch) issue(jb, stg);
     if constexpr (kDouble) {
       // first tile into buffer 0, the second one's loads in flight
-      tile_commit<T, D, W, APPEND>(a, bt, hk, c_begin * KC, jmax, stg, k_lds, v_lds, ap);
-      tile_issue<T, D, W, APPEND, U>(a, bt, hk, c_begin * KC + KT, jmax, stg, ap);
+      tile_commit<T, D, W, APPEND>(a, bt, hk, jb, jmax, stg, k_lds, v_lds, ap);
+      issue(jb + KT, stg);
     }
     ChunkState<D, NT> st;
+    // One tile.  `ready`: the register stage holding the next tile to commit,
+    // refilled with the tile after it (kPrefetch).
+    auto tile = [&](int j0, TileStage<T, D, W>& ready) {
+      __syncthreads();
+      if constexpr (kDouble) {
+        // tile j0 is in buffer (j0 / KT) & 1; the other one is free: stage tile j0 + KT there
+        const int cur = (j0 / KT) & 1;
+        if constexpr (!kLateCommit) {
+          unsigned char* const nk = lds + (cur ^ 1) * G_::BYTES;
+          tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, ready, nk, nk + G_::KBYTES, ap);
+        }
+        k_lds = lds + cur * G_::BYTES;
+        v_lds = k_lds + G_::KBYTES;
+      } else {
+        if constexpr (kPrefetch)
+          tile_commit<T, D, W, APPEND>(a, bt, hk, j0, jmax, ready, k_lds, v_lds, ap);
+        else
+          load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
+        __syncthreads();
+      }
+      const int jn = j0 + (kDouble ? 2 : 1) * KT;
+      auto mid = [&] {
+        if constexpr (kPrefetch) {
+          if constexpr (kLateCommit) {
+            unsigned char* const nk = lds + (((j0 / KT) & 1) ^ 1) * G_::BYTES;
+            tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, ready, nk, nk + G_::KBYTES, ap);
+          }
+          issue(jn, ready);
+        }
+      };
+      if (kSkipDead && !live) {  // no column of this wave exists: only its share of the tile loads
+        mid();
+        return;
+      }
+      f32x4 s[NT][KT / 16];
+      if constexpr (NT == 1) {
+        qk_tile_lds<T, D>(k_lds, q[0], s[0]);  // one M tile of K operands live at a time
+      } else {
+#if PKV_QK_PER_MT
+        qk_tiles_lds<T, D, NT>(k_lds, q, s);   // one M tile of K operands, all column groups
+#else
+        KOps<T, D> kop;
+        k_operands_lds<T, D>(k_lds, kop);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
+#endif
+      }
+      if constexpr (kPrefetch) {
+        // V operands two P.V steps ahead where registers allow (scalar block ids)
+        softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0, true, U ? 2 : 1>(st, s, lim, j0, a.mul, v_lds, mid);
+      } else {
+        softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
+      }
+    };
     for (int c = c_begin; c < c_end; ++c) {
       chunk_reset(st);
       const int jend = min((c + 1) * KC, jmax);
-      for (int j0 = c * KC; j0 < jend; j0 += KT) {
-        __syncthreads();
-        if constexpr (kDouble) {
-          // tile j0 is in buffer (j0 / KT) & 1; the other one is free: stage tile j0 + KT there
-          const int cur = (j0 / KT) & 1;
-          if constexpr (!kLateCommit) {
-            unsigned char* const nk = lds + (cur ^ 1) * G_::BYTES;
-            tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, stg, nk, nk + G_::KBYTES, ap);
-          }
-          k_lds = lds + cur * G_::BYTES;
-          v_lds = k_lds + G_::KBYTES;
-        } else {
-          if constexpr (kPrefetch)
-            tile_commit<T, D, W, APPEND>(a, bt, hk, j0, jmax, stg, k_lds, v_lds, ap);
-          else
-            load_tile<T, D, W, APPEND, U>(a, bt, hk, j0, jmax, k_lds, v_lds, ap);
-          __syncthreads();
-        }
-        f32x4 s[NT][KT / 16];
-        if constexpr (NT == 1) {
-          qk_tile_lds<T, D>(k_lds, q[0], s[0]);  // one M tile of K operands live at a time
-        } else {
-#if PKV_QK_PER_MT
-          qk_tiles_lds<T, D, NT>(k_lds, q, s);   // one M tile of K operands, all column groups
-#else
-          KOps<T, D> kop;
-          k_operands_lds<T, D>(k_lds, kop);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
-#endif
-        }
-        if constexpr (kPrefetch) {
-          const int jn = kDouble ? j0 + 2 * KT : j0 + KT;
-          // V operands two P.V steps ahead where registers allow (scalar block ids)
-          softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0, true, U ? 2 : 1>(
-              st, s, lim, j0, a.mul, v_lds, [&] {
-                if constexpr (kLateCommit) {
-                  unsigned char* const nk = lds + (((j0 / KT) & 1) ^ 1) * G_::BYTES;
-                  tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, stg, nk, nk + G_::KBYTES, ap);
-                }
-                tile_issue<T, D, W, APPEND, U>(a, bt, hk, jn, jmax, stg, ap);
-              });
-        } else {
-          softmax_pv_tile<T, D, NT, PKV_FULL_PIN != 0>(st, s, lim, j0, a.mul, v_lds);
-        }
-      }
+      for (int j0 = c * KC; j0 < jend; j0 += KT) tile(j0, stg);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float lc = column_sum(st.l[nt]);
@@ -1118,6 +1154,13 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
     } else {
       hipLaunchKernelGGL((attn_kernel<T, D, 1, 1, true, APPEND, false>), grid, dim3(64), 0, stream, a);
     }
+  } else if constexpr (PKV_SPLIT_W == 8) {
+    // 8 waves x kSplitGroups/2 column groups: the same columns per work group
+    constexpr int NT8 = kSplitGroups / 2;
+    if (uni)
+      hipLaunchKernelGGL((attn_kernel<T, D, 8, NT8, true, APPEND, true>), grid, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<T, D, 8, NT8, true, APPEND, false>), grid, dim3(512), 0, stream, a);
   } else if (uni) {
     hipLaunchKernelGGL((attn_kernel<T, D, 4, kSplitGroups, true, APPEND, true>), grid, dim3(256), 0, stream, a);
   } else {

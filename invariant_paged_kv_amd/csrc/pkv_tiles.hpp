@@ -164,9 +164,30 @@ struct TileStage {
   typename KvRaw<T>::type k[PER], v[PER];
 };
 
-template <class T, int D, int W, bool APPEND, bool U>
+// Block ids of a tile's row groups fetched one tile ahead of the loads that
+// use them (U only): lane i < PER holds the id of the wave's i-th row group.
+// A vector load, issued right after the previous tile's K/V loads, so the wait
+// for it comes where those loads are waited for anyway; a scalar id load
+// issued together with the K/V loads put the table's latency in front of
+// every tile's loads.
+struct TileIds {
+  uint32_t v = 0;
+};
+
+template <class T, int D, int W, bool U>
+__device__ __forceinline__ void tile_ids_fetch(const AttnArgs& a, const int32_t* bt, int j0, int jmax, TileIds& ids) {
+  if constexpr (U) {
+    using G_ = TileGeom<T, D>;
+    constexpr int PER = TileStage<T, D, W>::PER;
+    const int i = min(lane_id(), PER - 1);
+    const int g0 = ((static_cast<int>(threadIdx.x) & ~63) + i * 64 * W) / G_::CPR & ~15;
+    ids.v = static_cast<uint32_t>(bt[div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift)]);
+  }
+}
+
+template <class T, int D, int W, bool APPEND, bool U, bool kFetched = false>
 __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
-                                           TileStage<T, D, W>& stg, const Append& ap) {
+                                           TileStage<T, D, W>& stg, const Append& ap, const TileIds& ids = {}) {
   using G_ = TileGeom<T, D>;
   constexpr int PER = TileStage<T, D, W>::PER;
   const unsigned char* kb = static_cast<const unsigned char*>(a.k);
@@ -181,7 +202,10 @@ __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt,
       const int row = (threadIdx.x + i * 64 * W) / G_::CPR;
       const int g0 = __builtin_amdgcn_readfirstlane(row) & ~15;
       const int bi = div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift);
-      ublk[i] = static_cast<uint32_t>(((cint*)bt)[bi]);
+      if constexpr (kFetched)
+        ublk[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ids.v), i));
+      else
+        ublk[i] = static_cast<uint32_t>(((cint*)bt)[bi]);
       ubase[i] = bi * a.bs;
     }
   }
