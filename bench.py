@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--profile", choices=["decode", "prefill", "rescore", "chunked17", "backward", "fp8"],
+                    help="run one workload a few times and print its time (for rocprofv3); no JSON line")
+    ap.add_argument("--calls", type=int, default=5, help="calls of the --profile workload")
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--seqlen-k", type=int, default=131072)
     return ap.parse_args()
@@ -70,6 +73,9 @@ def main():
     import invariant_paged_kv_amd as pkv
     import pkv_inputs as gen
 
+    if args.profile:
+        profile_run(torch, pkv, gen, args.profile, args.calls)
+        return
     dev = "cuda"
     B, HQ, HK, D, BS = args.batch, 64, 8, 128, 256
     N = args.seqlen_k
@@ -241,6 +247,65 @@ def main():
         result["cpu_baseline"], result["oracle_parity"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale,
                                                                        out, lse)
     print(json.dumps(result), flush=True)
+
+
+def profile_run(torch, pkv, gen, what: str, calls: int):
+    """One workload, `calls` times after one untimed call, for a profiler: the
+    long-context decode call, the 8 x 8192 causal prefill, the 64-row re-score
+    over 131072 keys, the 17-token chunked prefill (one graph replay), the
+    prefill's backward, or the FP8 decode call."""
+    dev = "cuda"
+    if what in ("decode", "rescore", "fp8"):
+        B, HQ, HK, D, BS, N = 16, 64, 8, 128, 256, 131072
+        nb = gen.pool_num_blocks(N, BS, B)
+        dt = "fp8" if what == "fp8" else "bf16"
+        g = torch.Generator(device=dev).manual_seed(1005)
+        pool = gen.new_pool(nb, BS, HK, D, dt, "interleaved", device=dev, generator=g)
+        bt = gen.randperm_block_table(nb, B, generator=torch.Generator().manual_seed(1005)).to(dev)
+        rows = 64 if what == "rescore" else 1
+        q = gen.randn((B * rows, HQ, D), "bf16", generator=g, device=dev)
+        sk = torch.full((B,), N, dtype=torch.int32, device=dev)
+        cu = torch.arange(0, B * rows + 1, rows, dtype=torch.int32, device=dev)
+        ws = torch.empty(max(256, pkv.workspace_size(q, pool.k, pool.v, bt, max_seqlen_q=rows, max_seqlen_k=N)),
+                         dtype=torch.uint8, device=dev)
+        ks, vs = (0.5, 1.25) if dt == "fp8" else (1.0, 1.0)
+
+        def fn():
+            pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu, True, 1 / math.sqrt(D), max_seqlen_q=rows,
+                             max_seqlen_k=N, workspace=ws, k_scale=ks, v_scale=vs)
+    else:
+        B, HQ, HK, D, BS, S = 8, 16, 4, 128, 16, 8192
+        nb = gen.pool_num_blocks(S, BS, B)
+        g = torch.Generator(device=dev).manual_seed(1004)
+        pool = gen.new_pool(nb, BS, HK, D, "bf16", "contiguous", device=dev, generator=g)
+        bt = gen.randperm_block_table(nb, B, generator=torch.Generator().manual_seed(1004)).to(dev)
+        q = gen.randn((B * S, HQ, D), "bf16", generator=g, device=dev)
+        sk = torch.full((B,), S, dtype=torch.int32, device=dev)
+        cu = torch.arange(0, B * S + 1, S, dtype=torch.int32, device=dev)
+        scale = 1 / math.sqrt(D)
+        out, lse = pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu, True, scale, max_seqlen_q=S, max_seqlen_k=S)
+        if what == "prefill":
+            def fn():
+                pkv.attn_forward(q, pool.k, pool.v, bt, sk, cu, True, scale, max_seqlen_q=S, max_seqlen_k=S,
+                                 out=out, lse=lse)
+        elif what == "backward":
+            dout = gen.randn((B * S, HQ, D), "bf16", generator=g, device=dev)
+
+            def fn():
+                pkv.attn_backward(q, pool.k, pool.v, bt, sk, cu, True, scale, out, lse, dout, max_seqlen_q=S,
+                                  max_seqlen_k=S, total_k=B * S,
+                                  cu_seqlens_k=torch.arange(0, B * S + 1, S, dtype=torch.int32, device=dev))
+        else:   # chunked17: one replay of the captured 482-call graph
+            res = bench_chunked_prefill(torch, pkv, pool, bt, q, out, lse, S, scale, 17, reps=calls)
+            print(f"profile chunked17: {res['ms']} ms per replay, bitwise {res['bitwise_eq_one_shot']}", flush=True)
+            return
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        fn()
+    torch.cuda.synchronize()
+    print(f"profile {what}: {(time.perf_counter() - t0) * 1e3 / calls:.4f} ms per call (wall)", flush=True)
 
 
 FLUSH_BYTES = 1 << 30   # > L2 (8 x 4 MB) + the 256 MB Infinity Cache

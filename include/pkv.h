@@ -338,6 +338,10 @@ int pkv_validate_layout(const pkv_layout* kv_strides);
  *                         1024 and the keys reach 16384, else 2), 1 pipelined 8 waves x
  *                         16 columns per work group, 2 4 waves x 32 columns, 3 8 waves x
  *                         32 columns (not for the fused append, which takes 2)
+ *   PKV_OPT_DECODE_ORDER  one-wave decode kernels: dispatch order of the work items, 0 auto
+ *                         (2 when the grid has at most 2048 work items and each (sequence,
+ *                         KV head) at least 4 of them, else 1), 1 the items of one
+ *                         (sequence, KV head) consecutive, 2 the sequence fastest
  *   PKV_OPT_DEBUG         0 off, 1 debug mode: every call first enqueues a check of
  *                         its index data (the device-data preconditions above) on its
  *                         stream; when one fails, the call's kernels return without
@@ -349,7 +353,13 @@ int pkv_validate_layout(const pkv_layout* kv_strides);
  *                         on a device clears the word synchronously: make it outside
  *                         stream capture.
  */
-enum pkv_option { PKV_OPT_PATH = 1, PKV_OPT_SPLIT_CHUNKS = 2, PKV_OPT_FULL_KERNEL = 3, PKV_OPT_DEBUG = 4 };
+enum pkv_option {
+  PKV_OPT_PATH = 1,
+  PKV_OPT_SPLIT_CHUNKS = 2,
+  PKV_OPT_FULL_KERNEL = 3,
+  PKV_OPT_DEBUG = 4,
+  PKV_OPT_DECODE_ORDER = 5
+};
 int pkv_set_option(int option, int64_t value);
 int64_t pkv_get_option(int option);
 

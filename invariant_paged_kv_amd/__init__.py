@@ -28,7 +28,7 @@ PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_ALIGN, PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_OPTION = \
     0, -1, -2, -3, -4, -5, -6, -7
 PKV_ERR_DEVICE_DATA = -8
-PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL, PKV_OPT_DEBUG = 1, 2, 3, 4
+PKV_OPT_PATH, PKV_OPT_SPLIT_CHUNKS, PKV_OPT_FULL_KERNEL, PKV_OPT_DEBUG, PKV_OPT_DECODE_ORDER = 1, 2, 3, 4, 5
 PKV_CHECK_ATTENTION, PKV_CHECK_APPEND, PKV_CHECK_CACHE_WRITE = 0, 1, 2
 CHUNK_KEYS = 1024
 TILE_KEYS = 64
@@ -615,8 +615,11 @@ class options:
     """Context manager that sets library options and restores them on exit."""
 
     def __init__(self, path: Optional[int] = None, split_chunks: Optional[int] = None,
-                 full_kernel: Optional[int] = None, debug: Optional[int] = None):
+                 full_kernel: Optional[int] = None, debug: Optional[int] = None,
+                 decode_order: Optional[int] = None):
         self._want = {}
+        if decode_order is not None:
+            self._want[PKV_OPT_DECODE_ORDER] = decode_order
         if debug is not None:
             self._want[PKV_OPT_DEBUG] = debug
         if path is not None:

@@ -42,6 +42,7 @@ thread_local char g_msg[512] = "";
 std::atomic<int64_t> g_opt_path{0};
 std::atomic<int64_t> g_opt_split_chunks{0};
 std::atomic<int64_t> g_opt_full_kernel{0};
+std::atomic<int64_t> g_opt_decode_order{0};
 // Debug mode: PKV_OPT_DEBUG, initially on when the environment sets PKV_DEBUG to a nonzero value.
 int64_t env_debug() {
   const char* e = std::getenv("PKV_DEBUG");
@@ -372,6 +373,18 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.job_pref = p.lp.lpt ? reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + p.off_jobs) : nullptr;
   a.nbatch = l->batch;
   a.nhk = l->num_heads_k;
+  {
+    // One-wave decode kernels: sequence-fastest dispatch for grids of at most
+    // two rounds of wave slots whose (sequence, KV head) pairs span at least 4
+    // work items; in one process, same bits, against items-consecutive order:
+    // 64 x 4096 keys (Hq 16 / Hkv 4) 0.1095 -> 0.1002 ms, 16 x 16384 0.1166 ->
+    // 0.1058, 8 x 32768 (32 / 8) 0.2191 -> 0.2106, 4 x 65536 (64 / 8) 0.2250 ->
+    // 0.2153; 32 x 2048 (2 items) 0.0622 -> 0.0654 and 16 x 131072 (16384
+    // work items) 1.4603 -> 1.4776 keep the items-consecutive order.
+    const int64_t o = g_opt_decode_order.load();
+    const int64_t total = static_cast<int64_t>(l->batch) * l->num_heads_k * p.ncb * p.lp.items;
+    a.dorder = o == 0 ? (total <= 2048 && p.lp.items >= 4 ? 1 : 0) : static_cast<int32_t>(o - 1);
+  }
   rc = debug_check(check_limits(*l, append ? pkv::kOpAppend : pkv::kOpAttention, l->total_q), cu_seqlens_q,
                    seqlens_k, block_table, nullptr, stream, &a.dbg_word);
   if (rc) {
@@ -779,6 +792,10 @@ int pkv_set_option(int option, int64_t value) {
       if (value < 0 || value > 1) return fail(PKV_ERR_OPTION, "PKV_OPT_DEBUG must be 0 or 1");
       g_opt_debug.store(value);
       return ok();
+    case PKV_OPT_DECODE_ORDER:
+      if (value < 0 || value > 2) return fail(PKV_ERR_OPTION, "PKV_OPT_DECODE_ORDER must be 0, 1 or 2");
+      g_opt_decode_order.store(value);
+      return ok();
     default:
       return fail(PKV_ERR_OPTION, "unknown option %d", option);
   }
@@ -790,6 +807,7 @@ int64_t pkv_get_option(int option) {
     case PKV_OPT_SPLIT_CHUNKS: return g_opt_split_chunks.load();
     case PKV_OPT_FULL_KERNEL: return g_opt_full_kernel.load();
     case PKV_OPT_DEBUG: return g_opt_debug.load();
+    case PKV_OPT_DECODE_ORDER: return g_opt_decode_order.load();
     default: return -1;
   }
 }

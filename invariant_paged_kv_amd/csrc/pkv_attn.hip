@@ -403,6 +403,32 @@ __device__ __forceinline__ bool decode_job(const AttnArgs& a, int x, int& b, int
   return true;
 }
 
+// The (sequence, KV head, column block, item) of a one-wave decode work group
+// of the plain grid (x: column block and item, y: KV head, z: sequence), in
+// one of two dispatch orders (work groups go round-robin over the 8 XCDs):
+//   0  consecutive work groups run consecutive items of one (sequence, KV
+//      head) -- the faster order for grids of many rounds of wave slots (16 x
+//      131072 keys: 1.541 against 1.582 ms with order 1)
+//   1  the sequence fastest, then the item, then the KV head -- faster for
+//      grids of one or two rounds (64 x 4096 keys: 0.1058 against 0.1133 ms)
+// Orders that put the KV heads of one chunk next to each other, or on one
+// XCD, measured 4-16% slower on both.  Same (sequence, head, item) jobs in
+// every order, so the order changes no bit.
+__device__ __forceinline__ void decode_item(const AttnArgs& a, int& b, int& hk, int& cb, int& item) {
+  int x = blockIdx.x;
+  b = blockIdx.z;
+  hk = blockIdx.y;
+  if (a.dorder == 1) {
+    const int X = gridDim.x, B = gridDim.z;
+    const int lin = blockIdx.x + X * (blockIdx.y + gridDim.y * blockIdx.z);
+    b = lin % B;
+    x = (lin / B) % X;
+    hk = lin / (B * X);
+  }
+  cb = x % a.ncb;
+  item = x / a.ncb;
+}
+
 // ---------------------------------------------------------------------------
 // Decode split kernel: one wave per work item (sequence, KV head, 16 columns,
 // run of chunks), for up to 16 query columns per KV head (g * L <= 16).
@@ -781,10 +807,8 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   // head): concurrently running waves then read different cache blocks
   // (ordering the KV heads of one chunk next to each other measured ~9%
   // slower on the long-context workload).
-  int b = blockIdx.z;
-  int hk = blockIdx.y;
-  int cb = blockIdx.x % a.ncb;
-  int item = blockIdx.x / a.ncb;
+  int b, hk, cb, item;
+  decode_item(a, b, hk, cb, item);
   if (a.job_pref) {  // longest-first job list (one column block, one chunk per item)
     cb = 0;
     if (!decode_job(a, blockIdx.x, b, hk, item)) return;
@@ -927,10 +951,8 @@ __global__ __launch_bounds__(64, T::KVB == 1 ? 2 : 1) void decode2_kernel(AttnAr
   using G_ = TileGeom<T, D>;
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
 
-  int b = blockIdx.z;
-  int hk = blockIdx.y;
-  int cb = blockIdx.x % a.ncb;
-  int item = blockIdx.x / a.ncb;
+  int b, hk, cb, item;
+  decode_item(a, b, hk, cb, item);
   if (a.job_pref) {  // longest-first job list (one column block, one chunk per item)
     cb = 0;
     if (!decode_job(a, blockIdx.x, b, hk, item)) return;

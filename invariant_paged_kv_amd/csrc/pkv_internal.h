@@ -53,6 +53,9 @@ struct AttnArgs {
   // Debug mode: the device error word the call's check kernel wrote; every
   // kernel of the call returns at once when it is nonzero.  NULL otherwise.
   const int32_t* dbg_word;
+  // One-wave decode kernels, plain grid: dispatch order of the work items
+  // (0: items of one (sequence, KV head) consecutive; 1: sequence fastest).
+  int32_t dorder;
 };
 
 struct MergeArgs {

@@ -114,3 +114,38 @@ def test_longest_first_order_with_empty_sequences():
         r = case.cu[b]
         assert torch.all(lse[r] == -math.inf) and torch.all(out[r] == 0), b
     gc.check_oracle(case, out, lse, seq_ids=[0, 4, 7, 9, 31])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("shape", [(16, 16, 4, 16, 5000), (24, 32, 8, 256, 6000), (40, 8, 2, 24, 3000)])
+def test_dispatch_orders_keep_bits(dtype, shape):
+    """Both dispatch orders of the plain decode grid (items of one (sequence,
+    KV head) consecutive, or the sequence fastest) run the same jobs: same bits,
+    for both one-wave decode kernels (a grid within one round of wave slots and
+    one beyond it), and the oracle on two sequences."""
+    B, hq, hk, bs, n = shape
+    announce(f"decode dispatch orders {dtype} {shape}")
+    case = gc.make_case(9800 + B, "bf16", B, hq, hk, 128, bs, n, "interleaved", True, [1] * B)
+    kw = {}
+    if dtype == "fp8":
+        g = torch.Generator().manual_seed(9801 + B)
+        case.pool = gc.to_device(gen.new_pool(gen.pool_num_blocks(n, bs, B), bs, hk, 128, "fp8", "interleaved",
+                                              generator=g))
+        kw = dict(k_scale=0.5, v_scale=1.25)
+    res = []
+    for order in (1, 2):
+        with pkv.options(decode_order=order):
+            o = gc.nan_outputs(case.q)
+            out, lse = pkv.attn_forward(case.q, case.pool.k, case.pool.v, case.block_table, case.seqlens_d(),
+                                        case.cu_d(), True, case.scale, max_seqlen_q=1,
+                                        max_seqlen_k=case.max_seqlen_k, **o, **kw)
+            torch.cuda.synchronize()
+            res.append((out, lse))
+    gc.assert_bitwise(res[0], res[1], "dispatch order 1 vs 2")
+    with pkv.options(path=2):
+        full = pkv.attn_forward(case.q, case.pool.k, case.pool.v, case.block_table, case.seqlens_d(), case.cu_d(),
+                                True, case.scale, max_seqlen_q=1, max_seqlen_k=case.max_seqlen_k, **kw)
+    torch.cuda.synchronize()
+    gc.assert_bitwise(res[0], full, "decode vs full path")
+    if dtype == "bf16":
+        gc.check_oracle(case, *res[0], seq_ids=[0, B - 1])
