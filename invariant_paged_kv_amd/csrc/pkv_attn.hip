@@ -1124,9 +1124,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 template <class T, int D, bool APPEND>
 static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStream_t stream) {
   // Uniform block ids per 16 rows (block size a multiple of 16) with 32-bit
-  // in-block offsets: scalar id loads and scalar-based addresses.
+  // in-block offsets and block strides below 2^32 bytes: scalar id loads and
+  // scalar-based addresses.
   const int64_t span = (static_cast<int64_t>(a.bs) - 1) * std::max(a.kss, a.vss) * T::KVB + D * T::KVB;
-  const bool uni = a.bs % 16 == 0 && a.kss >= 0 && a.vss >= 0 && span < (int64_t{1} << 31);
+  const bool uni = a.bs % 16 == 0 && a.kss >= 0 && a.vss >= 0 && span < (int64_t{1} << 31) && a.kbs >= 0 &&
+                   a.vbs >= 0 && std::max(a.kbs, a.vbs) * T::KVB < (int64_t{1} << 32);
   if (pl.full) {
     dim3 grid(a.ncb, pl.hk, pl.batch);
     if constexpr (T::EB == 2 && !APPEND) {

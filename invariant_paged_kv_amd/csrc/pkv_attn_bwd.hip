@@ -585,7 +585,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a_in, const BwdPlan& pl, hipStream
       // scalar block ids per 16 rows when the block size allows (as the forward's tile loader)
       const AttnArgs& f = a.f;
       const int64_t span = (static_cast<int64_t>(f.bs) - 1) * std::max(f.kss, f.vss) * T::KVB + D * T::KVB;
-      const bool uni = f.bs % 16 == 0 && f.kss >= 0 && f.vss >= 0 && span < (int64_t{1} << 31);
+      const bool uni = f.bs % 16 == 0 && f.kss >= 0 && f.vss >= 0 && span < (int64_t{1} << 31) && f.kbs >= 0 &&
+                       f.vbs >= 0 && std::max(f.kbs, f.vbs) * T::KVB < (int64_t{1} << 32);
       const dim3 grid(a.f.ncb, pl.hk, pl.batch);
       if (uni)
         hipLaunchKernelGGL((bwd_dq_kernel<T, D, W, NT, true>), grid, dim3(64 * W), 0, stream, a);

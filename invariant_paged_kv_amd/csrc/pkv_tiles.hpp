@@ -61,7 +61,8 @@ __device__ __forceinline__ void kv_store_new(const Append& ap, bool in, int jc, 
 // key row (16 stored bytes, or 8 FP8 bytes widened to 16).  The block address
 // uses the real block stride (contiguous or K/V-interleaved caches alike).
 // Keys >= jmax are not read; their rows are zero.
-// U (block size a multiple of 16, in-block offsets below 2^31 bytes): the rows
+// U (block size a multiple of 16, in-block offsets below 2^31 bytes, block
+// strides below 2^32 bytes): the rows
 // one wave loads with one instruction lie in one 16-row group, hence in one
 // cache block; its id is a scalar load and the address a scalar block base
 // plus a 32-bit lane offset, instead of a per-lane table lookup and 64-bit
@@ -209,6 +210,12 @@ __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt,
       ubase[i] = bi * a.bs;
     }
   }
+  // U: block strides below 2^32 bytes, so a block's base offset is one
+  // 32 x 32-bit product (measured 3% faster on the 8 x 8192 prefill than the
+  // 64-bit product)
+  const uint32_t kbsb = static_cast<uint32_t>(a.kbs) * T::KVB, vbsb = static_cast<uint32_t>(a.vbs) * T::KVB;
+  const unsigned char* const kbh = kb + (int64_t)hk * a.khs * T::KVB;
+  const unsigned char* const vbh = vb + (int64_t)hk * a.vhs * T::KVB;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int qi = threadIdx.x + i * 64 * W;
@@ -219,11 +226,8 @@ __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt,
     const unsigned char* vc;
     if constexpr (U) {
       const int slot = jc - ubase[i];
-      const int64_t blk = static_cast<int64_t>(static_cast<uint64_t>(ublk[i]));
-      kc = kb + (blk * a.kbs + (int64_t)hk * a.khs) * T::KVB +
-           static_cast<uint32_t>(slot * static_cast<int>(a.kss) * T::KVB + off);
-      vc = vb + (blk * a.vbs + (int64_t)hk * a.vhs) * T::KVB +
-           static_cast<uint32_t>(slot * static_cast<int>(a.vss) * T::KVB + off);
+      kc = kbh + static_cast<uint64_t>(ublk[i]) * kbsb + static_cast<uint32_t>(slot * static_cast<int>(a.kss) * T::KVB + off);
+      vc = vbh + static_cast<uint64_t>(ublk[i]) * vbsb + static_cast<uint32_t>(slot * static_cast<int>(a.vss) * T::KVB + off);
     } else {
       const int bi = div_block(jc, a.bs_mul, a.bs_shift);
       const int64_t blk = bt[bi];
@@ -269,22 +273,25 @@ __device__ __forceinline__ void tile_commit(const AttnArgs& a, const int32_t* bt
     kr[i] = kv_widen<T>(stg.k[i]);
     vr[i] = kv_widen<T>(stg.v[i]);
   }
+  // piece i of this lane is tile row row0 + i * STEP, 16-byte part `part`
+  constexpr int STEP = 64 * W / G_::CPR;
+  static_assert(STEP * G_::CPR == 64 * W, "a work group's pieces cover whole rows");
+  const int row0 = threadIdx.x / G_::CPR, part = threadIdx.x % G_::CPR;
   if (j0 + KT > jmax) {  // rows past jmax read as zero
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int row = (threadIdx.x + i * 64 * W) / G_::CPR;
-      if (j0 + row >= jmax) {
+      if (j0 + row0 + i * STEP >= jmax) {
         kr[i] = u32x4{0, 0, 0, 0};
         vr[i] = u32x4{0, 0, 0, 0};
       }
     }
   }
+  unsigned char* const kp = k_lds + row0 * G_::KPITCH + 16 * part;
+  unsigned char* const vp = v_lds + row0 * G_::VPITCH + 16 * part;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int qi = threadIdx.x + i * 64 * W;
-    const int row = qi / G_::CPR, part = qi % G_::CPR;
-    *reinterpret_cast<u32x4*>(k_lds + row * G_::KPITCH + 16 * part) = kr[i];
-    *reinterpret_cast<u32x4*>(v_lds + row * G_::VPITCH + 16 * part) = vr[i];
+    *reinterpret_cast<u32x4*>(kp + i * STEP * G_::KPITCH) = kr[i];
+    *reinterpret_cast<u32x4*>(vp + i * STEP * G_::VPITCH) = vr[i];
   }
 }
 
