@@ -78,6 +78,12 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #ifndef PKV_SPLIT_LATE_COMMIT
 #define PKV_SPLIT_LATE_COMMIT 1
 #endif
+#ifndef PKV_SPLIT_STAGGER
+#define PKV_SPLIT_STAGGER 1
+#endif
+#ifndef PKV_SPLIT_QK_ILP
+#define PKV_SPLIT_QK_ILP 1
+#endif
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND, bool U>
 __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a) {
@@ -104,7 +110,18 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
   // barrier that ended tile t-1, its last reader.
   constexpr bool kLateCommit = kDouble && SPLIT && PKV_SPLIT_LATE_COMMIT;
   constexpr bool kSkipDead = SPLIT && PKV_SKIP_DEAD_WAVES != 0;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[(kDouble ? 2 : 1) * G_::BYTES];
+  // Split kernel, 8 waves x 16 columns: the odd waves run each tile's P.V
+  // one barrier interval late, at the start of the next tile, so that while
+  // the even waves read K for Q.K^T the odd ones read V, and their softmaxes
+  // fall at different times: the LDS reads of a tile are spread over the
+  // interval instead of coming in two bursts from every wave at once.  The
+  // tile buffers rotate over three (the tile being computed, the one whose
+  // late P.V is still to come, the one being staged).  Each column's
+  // operations keep their order (softmax t, P.V t, softmax t+1), so the bits
+  // are those of the unstaggered kernel.
+  constexpr bool kStagger = kLateCommit && NT == 1 && W == 8 && PKV_SPLIT_STAGGER != 0;
+  constexpr int kBufs = kStagger ? 3 : (kDouble ? 2 : 1);
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kBufs * G_::BYTES];
   unsigned char* k_lds = lds;
   unsigned char* v_lds = lds + G_::KBYTES;
 
@@ -213,9 +230,27 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
     ChunkState<D, NT> st;
     // One tile.  `ready`: the register stage holding the next tile to commit,
     // refilled with the tile after it (kPrefetch).
+    // kStagger: an odd wave's P.V of its previous tile, still to be done
+    const bool late = kStagger && (wave & 1) != 0;
+    u32x4 pb_late[NT][KT / 32];
+    const unsigned char* v_late = nullptr;
+    auto late_pv = [&] {
+      if constexpr (kStagger) {
+        if (late && v_late != nullptr) {
+          pv_part<T, D, NT, PKV_FULL_PIN != 0, U ? 2 : 1>(st, pb_late, v_late);
+          v_late = nullptr;
+        }
+      }
+    };
     auto tile = [&](int j0, TileStage<T, D, W>& ready) {
       __syncthreads();
-      if constexpr (kDouble) {
+      if constexpr (kStagger) {
+        // tile j0 in buffer ((j0 - jb) / KT) % 3 (the first one in buffer 0);
+        // tile j0 + KT is staged into the next one
+        const int cur = ((j0 - jb) / KT) % 3;
+        k_lds = lds + cur * G_::BYTES;
+        v_lds = k_lds + G_::KBYTES;
+      } else if constexpr (kDouble) {
         // tile j0 is in buffer (j0 / KT) & 1; the other one is free: stage tile j0 + KT there
         const int cur = (j0 / KT) & 1;
         if constexpr (!kLateCommit) {
@@ -235,7 +270,7 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
       auto mid = [&] {
         if constexpr (kPrefetch) {
           if constexpr (kLateCommit) {
-            unsigned char* const nk = lds + (((j0 / KT) & 1) ^ 1) * G_::BYTES;
+            unsigned char* const nk = lds + (kStagger ? ((j0 - jb) / KT + 1) % 3 : ((j0 / KT) & 1) ^ 1) * G_::BYTES;
             tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, ready, nk, nk + G_::KBYTES, ap);
           }
           issue(jn, ready);
@@ -245,8 +280,11 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
         mid();
         return;
       }
+      late_pv();
       f32x4 s[NT][KT / 16];
-      if constexpr (NT == 1) {
+      if constexpr (NT == 1 && SPLIT && W == 8 && T::EB == 2 && PKV_SPLIT_QK_ILP) {
+        qk_tile_lds_ilp<T, D>(k_lds, q[0], s[0]);  // registers to spare: all K operands, chains interleaved
+      } else if constexpr (NT == 1) {
         qk_tile_lds<T, D>(k_lds, q[0], s[0]);  // one M tile of K operands live at a time
       } else {
 #if PKV_QK_PER_MT
@@ -257,6 +295,14 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) qk_tile<T, D>(kop, q[nt], s[nt]);
 #endif
+      }
+      if constexpr (kStagger) {
+        if (late) {
+          softmax_part<T, D, NT>(st, s, lim, j0, a.mul, pb_late);
+          mid();
+          v_late = v_lds;
+          return;
+        }
       }
       if constexpr (kPrefetch) {
         // V operands two P.V steps ahead where registers allow (scalar block ids)
@@ -269,6 +315,7 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
       chunk_reset(st);
       const int jend = min((c + 1) * KC, jmax);
       for (int j0 = c * KC; j0 < jend; j0 += KT) tile(j0, stg);
+      late_pv();  // the chunk's last P.V (its buffer is not restaged before two more tiles)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float lc = column_sum(st.l[nt]);

@@ -265,6 +265,24 @@ __device__ __forceinline__ void qk_tile_lds(const unsigned char* k_lds, const QO
   }
 }
 
+// QK^T for one tile with all K operands read first and the M tiles' MFMA
+// chains interleaved (k outer, M tile inner): each accumulator sees the
+// qk_tile chain, but consecutive MFMAs are independent.
+template <class T, int D>
+__device__ __forceinline__ void qk_tile_lds_ilp(const unsigned char* k_lds, const QOps<T, D>& q,
+                                                f32x4 (&s)[KT / 16]) {
+  using G_ = TileGeom<T, D>;
+  static_assert(T::EB == 2, "bf16 compute type");
+  KOps<T, D> kop;
+  k_operands_lds<T, D>(k_lds, kop);
+#pragma unroll
+  for (int mt = 0; mt < G_::MT; ++mt) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < G_::NK; ++k)
+#pragma unroll
+    for (int mt = 0; mt < G_::MT; ++mt) s[mt] = mfma_bf16(kop[mt][k], q.v[k], s[mt]);
+}
+
 // QK^T of NT column groups with the K operands read from LDS one M tile at a
 // time, each M tile's operands serving every group (the qk_tile chain per group).
 template <class T, int D, int NT>
@@ -469,13 +487,15 @@ __device__ __forceinline__ void pv_part(ChunkState<D, NT>& st, const u32x4 (&pb)
       constexpr int NS = G_::DT * KS;
       u32x4 vq[kAhead];
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) vq[i] = v_operand_bf16(v_lds, G_::VPITCH, i % KS, i / KS);
+      for (int i = 0; i < kAhead; ++i) vq[i] = v_operand_bf16(v_lds, G_::VPITCH, i / G_::DT, i % G_::DT);
 #pragma unroll
       for (int step = 0; step < NS; ++step) {
-        const int dt = step / KS, ks = step % KS;
+        // ks outer: consecutive MFMAs go to different d-tiles (each d-tile
+        // still takes its steps in ascending ks; 1-2% faster than dt outer)
+        const int dt = step % G_::DT, ks = step / G_::DT;
         const u32x4 va = vq[step % kAhead];
         if (step + kAhead < NS)
-          vq[step % kAhead] = v_operand_bf16(v_lds, G_::VPITCH, (step + kAhead) % KS, (step + kAhead) / KS);
+          vq[step % kAhead] = v_operand_bf16(v_lds, G_::VPITCH, (step + kAhead) / G_::DT, (step + kAhead) % G_::DT);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) st.o[nt][dt] = mfma_bf16(va, pb[nt][ks], st.o[nt][dt]);
         __builtin_amdgcn_sched_barrier(0);
