@@ -6,6 +6,10 @@
 #include "pkv_device.hpp"
 #include "pkv_internal.h"
 
+#ifndef PKV_TILE_IDS_FAST
+#define PKV_TILE_IDS_FAST 1
+#endif
+
 namespace pkv {
 
 // Fused append: key positions >= n_old are this call's own rows and are read
@@ -198,17 +202,47 @@ __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt,
   if constexpr (U) {
     static_assert(64 % G_::CPR == 0 && 64 / G_::CPR <= 16, "a wave's rows must lie in one 16-row group");
     using cint = const __attribute__((address_space(4))) int32_t;
+    auto per_group = [&] {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int row = (threadIdx.x + i * 64 * W) / G_::CPR;
-      const int g0 = __builtin_amdgcn_readfirstlane(row) & ~15;
-      const int bi = div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift);
-      if constexpr (kFetched)
-        ublk[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ids.v), i));
-      else
-        ublk[i] = static_cast<uint32_t>(((cint*)bt)[bi]);
-      ubase[i] = bi * a.bs;
-    }
+      for (int i = 0; i < PER; ++i) {
+        const int row = (threadIdx.x + i * 64 * W) / G_::CPR;
+        const int g0 = __builtin_amdgcn_readfirstlane(row) & ~15;
+        const int bi = div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift);
+        if constexpr (kFetched)
+          ublk[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ids.v), i));
+        else
+          ublk[i] = static_cast<uint32_t>(((cint*)bt)[bi]);
+        ubase[i] = bi * a.bs;
+      }
+    };
+#if PKV_TILE_IDS_FAST
+    // A tile below jmax (no clamped rows): with a block size that is a
+    // multiple of the tile, the whole tile lies in one block (one id); with
+    // 16-key blocks and 16 rows between a lane's pieces (4 waves, 16 pieces
+    // per row), piece i of every wave lies in the tile's i-th block, so the
+    // ids are four consecutive table entries.
+    if constexpr (!kFetched) {
+      if (j0 + KT <= jmax && (a.bs & (KT - 1)) == 0) {
+        const int bi = div_block(j0, a.bs_mul, a.bs_shift);
+        const uint32_t id = static_cast<uint32_t>(((cint*)bt)[bi]);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          ublk[i] = id;
+          ubase[i] = bi * a.bs;
+        }
+      } else if (64 * W / G_::CPR == 16 && PER == KT / 16 && j0 + KT <= jmax && a.bs == 16) {
+        const int b0 = j0 >> 4;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          ublk[i] = static_cast<uint32_t>(((cint*)bt)[b0 + i]);
+          ubase[i] = (b0 + i) << 4;
+        }
+      } else {
+        per_group();
+      }
+    } else
+#endif
+      per_group();
   }
   // U: block strides below 2^32 bytes, so a block's base offset is one
   // 32 x 32-bit product (measured 3% faster on the 8 x 8192 prefill than the
