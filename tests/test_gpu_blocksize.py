@@ -5,9 +5,11 @@ The block size only decides where a key's row is stored (key j of a sequence
 sits in table entry j / block_size, slot j % block_size); it enters no
 arithmetic.  So for every path -- the split decode kernels, the 4-wave and
 8-wave full kernels and the 4-wave split kernel -- out and lse must be bitwise identical
-across block sizes.  The sizes cover both ways the kernels address a tile:
-multiples of 16 (one block id per 16-row group, read with a scalar load) and
-other sizes (a block id per row).  Slots the tables do not reference hold NaN,
+across block sizes.  The sizes cover every way the kernels address a tile:
+multiples of 16 (one block id per 16-row group, read with a scalar load; for
+a tile below the sequence's end, one id per tile when the block size is a
+multiple of the 64-key tile -- 64, 256 -- and four consecutive ids with
+16-key blocks) and other sizes (a block id per row).  Slots the tables do not reference hold NaN,
 and sequence lengths are not multiples of the tile, so a read of a wrong slot
 or a missed clamp at a sequence's end shows up as NaN or changed bits.  One
 configuration per dtype is also checked against the oracle.
