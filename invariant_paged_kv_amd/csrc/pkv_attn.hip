@@ -8,7 +8,9 @@
 //                             loaded straight into registers a tile ahead.
 //   decode2_kernel            the same with two tiles in flight: FP8 caches,
 //                             and bf16 when the grid exceeds 1024 work items.
-//   attn_kernel<SPLIT=true>   more columns (or fp32): 4 waves sharing LDS tiles.
+//   attn_kernel<SPLIT=true>   more columns (or fp32): 8 waves x 16 columns
+//                             sharing LDS tiles (bf16/FP8: three tile buffers,
+//                             the odd waves' P.V one tile late).
 //   decode_plan_kernel        ragged batches: prefix counts for the one-wave
 //                             kernels' longest-first job order.
 // Full (prefill) path: one work item per (sequence, KV head, column block)
