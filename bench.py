@@ -490,7 +490,7 @@ def measured_traffic():
 
     The counters (FETCH_SIZE, WRITE_SIZE, calibrated on a plain copy) were
     taken on specific kernel sources; if those have changed since, the figure
-    no longer describes this build and None is reported.
+    no longer describes the compiled library and None is reported.
     """
     import hashlib
     try:

@@ -8,7 +8,7 @@ deterministic training backward for causal prefill and chunked prefill that
 reports the gradients of the query, key and value tensors (dq, dk, dv) over
 the same forward graph, with decode backward unsupported.
 
-What is differentiated (readings listed in the design doc):
+What is differentiated (readings where the pages are silent):
 
 * The function is ``out`` of the forward (``paged_kv.attention``); its
   attention-domain ``lse`` is an auxiliary output whose cotangent is zero.

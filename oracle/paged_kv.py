@@ -23,7 +23,7 @@ Sources, cited by page title and section:
 * AstrAI commit list: queries of several requests are packed and addressed
   through cumulative query lengths.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * Causal alignment is bottom-right: with ``n`` visible keys and ``L`` query rows
   for a sequence, row ``r`` sits at key position ``n - L + r`` and sees keys
