@@ -143,14 +143,19 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 // LDS tiles.  A tile holds KT consecutive keys (tile-local row = key - j0) of
 // one KV head, row-major with a 16-byte pad per row.
 // ---------------------------------------------------------------------------
-// Row pitches are chosen for the LDS banks: K rows are read 16 bytes per lane
-// from 16 consecutive rows (a 16-byte pad spreads 8 rows over all banks); V
-// rows are read by ds_read_b64_tr_b16, 4 rows x 32 bytes per 16 lanes (a
-// 32-byte pad puts those 4 rows on disjoint banks).
+// Row pitches are chosen for the LDS banks: V rows are read by
+// ds_read_b64_tr_b16, 4 rows x 32 bytes per 16 lanes (a 32-byte pad puts
+// those 4 rows on disjoint banks).  K rows are read 16 bytes per lane from 16
+// consecutive rows, and by the backward's dq kernel also through the
+// transposing read; the same 32-byte pad measured faster than a 16-byte one
+// (same bits: 8 x 8192 prefill +0.8%, its backward +2.4%).
+#ifndef PKV_KPAD
+#define PKV_KPAD 32
+#endif
 template <class T, int D>
 struct TileGeom {
   static constexpr int ROW_BYTES = D * T::EB;          // 256 for bf16 d=128
-  static constexpr int KPITCH = ROW_BYTES + 16;        // bytes between K rows in LDS
+  static constexpr int KPITCH = ROW_BYTES + PKV_KPAD;  // bytes between K rows in LDS
   static constexpr int VPITCH = ROW_BYTES + 32;        // bytes between V rows in LDS
   static constexpr int CPR = ROW_BYTES / 16;           // 16-byte chunks per row
   static constexpr int KBYTES = KT * KPITCH;           // K tile
