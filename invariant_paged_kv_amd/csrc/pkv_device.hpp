@@ -353,13 +353,24 @@ __device__ __forceinline__ u32x4 v_operand_bf16(const unsigned char* v_lds, int 
 // xor partner pair, so both lanes of a pair combine the same two values in the
 // same operand order (max and add are commutative, so the bits equal those of
 // a shuffle-based butterfly).
+// max of two lane values after a permlane swap.  fmaxf would first quiet
+// each operand (two v_max_f32 x, x, which the compiler cannot prove
+// redundant for permlane results); the operands are arithmetic results, so
+// never signalling NaNs, and one v_max_f32 gives the value fmaxf would (same
+// bits; 8 fewer VALU instructions per 64-key tile of two column groups:
+// re-score +2.8%, prefill +0.9%, 17-token chunked prefill +1.5%).
+__device__ __forceinline__ float max_pair(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_pair(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_pair(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float add_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
