@@ -80,6 +80,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
 #ifndef PKV_SPLIT_LATE_COMMIT
 #define PKV_SPLIT_LATE_COMMIT 1
 #endif
+#ifndef PKV_JOB_SEARCH_WAVE
+#define PKV_JOB_SEARCH_WAVE 1
+#endif
 #ifndef PKV_SPLIT_STAGGER
 #define PKV_SPLIT_STAGGER 1
 #endif
@@ -434,12 +437,32 @@ __device__ __forceinline__ bool decode_job(const AttnArgs& a, int x, int& b, int
     pr = pp;
     if (m >= pp[a.nbatch] * H) return false;
   }
+#if PKV_JOB_SEARCH_WAVE
+  // The largest b with H * pr[b] <= m (pr nondecreasing, pr[0] = 0, H *
+  // pr[batch] > m) is the count of k in [1, batch] with H * pr[k] <= m: the
+  // wave counts 256 entries per round of loads (4 per lane, ballots) instead
+  // of one dependent scalar load per halving.
+  {
+    const int32_t* prv = a.job_pref + (pr == pf ? 0 : a.nbatch + 1);
+    const int lane = lane_id();
+    int cnt = 0;
+    for (int base = 1; base <= a.nbatch; base += 256) {
+      int v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = prv[min(base + 4 * lane + i, a.nbatch)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(base + 4 * lane + i <= a.nbatch && v[i] * H <= m));
+    }
+    b = cnt;
+  }
+#else
   int lo = 0, hi = a.nbatch;  // largest b with H * pr[b] <= m (pr[0] = 0, H * pr[batch] > m)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (pr[mid] * H <= m) lo = mid; else hi = mid;
   }
   b = lo;
+#endif
   const int r = m - pr[b] * H;
   if (pr == pf) {
     const int f = pf[b + 1] - pf[b];  // this sequence's full chunks, per KV head
@@ -1125,11 +1148,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int part = static_cast<int>(wg % WPR);
   if (w >= a.total_q * a.hq) return;
   const int64_t row = w / a.hq;
-  const int b = row_sequence(a.cu_q, a.batch, row);
-  if (b >= a.batch) return;
-  const int n = a.seqlens_k[b];
-  const int L = a.cu_q[b + 1] - a.cu_q[b];
-  const int p = n - L + static_cast<int>(row - a.cu_q[b]);
+  const SeqOfRow sr = seq_of_row(a.cu_q, a.seqlens_k, a.batch, row);
+  if (sr.b >= a.batch) return;
+  const int n = sr.n;
+  const int L = sr.cu1 - sr.cu0;
+  const int p = n - L + static_cast<int>(row - sr.cu0);
   const int lim = a.causal ? min(p + 1, n) : n;
   const int nck = lim > 0 ? min((lim + KC - 1) / KC, a.maxc) : 0;
   const int lane = lane_id();

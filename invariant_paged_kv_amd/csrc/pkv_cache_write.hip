@@ -32,9 +32,10 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, int 
   const int i0 = static_cast<int>(threadIdx.x);
   u32x4_cw first = {0, 0, 0, 0};
   if (i0 < npieces) first = *reinterpret_cast<const u32x4_cw*>(src_of(i0));
-  const int b = row_sequence(a.cu_new, a.batch, tok);
+  const SeqOfRow sr = seq_of_row(a.cu_new, a.seqlens_k, a.batch, tok);
+  const int b = sr.b;
   if (b >= a.batch) return;
-  const int pos = a.seqlens_k[b] + static_cast<int>(tok - a.cu_new[b]);
+  const int pos = sr.n + static_cast<int>(tok - sr.cu0);
   const int bi = div_block(pos, a.bs_mul, a.bs_shift);
   const int64_t blk = a.block_table[(int64_t)b * a.mbps + bi];
   const int64_t slot = pos - bi * a.bs;

@@ -150,6 +150,41 @@ __device__ __forceinline__ int row_sequence(const int32_t* cu, int batch, int64_
   return lo;
 }
 
+// row_sequence together with that sequence's row offsets cu[b], cu[b + 1]
+// and its length seqlens[b] (b < batch; with b == batch the row lies past the
+// last sequence and the other fields are unset).  For batches of up to 63
+// sequences every lane loads its own sequence's three values in the same
+// round as the probe, and the wave takes sequence b's from lane b: one round
+// of dependent loads instead of two.  Same whole-wave, uniform-row contract
+// as row_sequence.
+struct SeqOfRow {
+  int b, cu0, cu1, n;
+};
+__device__ __forceinline__ SeqOfRow seq_of_row(const int32_t* cu, const int32_t* seqlens, int batch, int64_t row) {
+  SeqOfRow r{batch, 0, 0, 0};
+  if (batch <= 0) return r;
+  if (batch < 64) {
+    const int lane = static_cast<int>(__lane_id());
+    const int c0 = cu[min(lane, batch)];          // lanes past the batch re-read the last entry
+    const int c1 = cu[min(lane + 1, batch)];
+    const int sn = seqlens[min(lane, batch - 1)];
+    r.b = __popcll(__ballot(lane < batch && c1 <= row));
+    if (r.b < batch) {
+      r.cu0 = __builtin_amdgcn_readlane(c0, r.b);
+      r.cu1 = __builtin_amdgcn_readlane(c1, r.b);
+      r.n = __builtin_amdgcn_readlane(sn, r.b);
+    }
+    return r;
+  }
+  r.b = row_sequence(cu, batch, row);
+  if (r.b < batch) {
+    r.cu0 = cu[r.b];
+    r.cu1 = cu[r.b + 1];
+    r.n = seqlens[r.b];
+  }
+  return r;
+}
+
 // Arguments of the backward kernels.  `f` carries the forward's inputs
 // (q, caches, table, lengths, strides, GQA factor, block-size divisor,
 // causal flag; f.mul is the score multiplier of the forward).

@@ -116,6 +116,37 @@ def test_longest_first_order_with_empty_sequences():
     gc.check_oracle(case, out, lse, seq_ids=[0, 4, 7, 9, 31])
 
 
+@pytest.mark.parametrize("batch", [63, 64, 300])
+def test_many_sequences_lookups(batch):
+    """The row -> sequence lookups of the merge and the append take every lane's own sequence
+    values in the probe's round below 64 sequences and a separate round from 64 on; the job list's
+    search counts 256 prefix entries per round (300 sequences x 8 KV heads x 2 chunks = 4800 jobs:
+    two rounds).  Same bits as the plain order and the full path, the oracle on sampled sequences,
+    and the appended rows exactly where host indexing puts them."""
+    announce(f"decode lookups, batch {batch}")
+    B, HK, D, BS = batch, 8, 128, 16
+    case = gc.make_case(9800 + batch, "bf16", B, 16, HK, D, BS, 2048, "interleaved", True, [1] * B)
+    out, lse = gc.run(case)
+    gc.assert_bitwise(gc.run(case, split_chunks=2), (out, lse), "plain order (2 chunks per item)")
+    gc.assert_bitwise(gc.run(case, path=2), (out, lse), "full path")
+    gc.check_oracle(case, out, lse, seq_ids=[0, B // 2, B - 1])
+    g = torch.Generator().manual_seed(9801 + batch)
+    kn = gen.randn((B, HK, D), "bf16", generator=g).to(gc.DEV)
+    vn = gen.randn((B, HK, D), "bf16", generator=g).to(gc.DEV)
+    sk = torch.tensor(case.seqlens, dtype=torch.int32, device=gc.DEV)
+    cu = torch.arange(B + 1, dtype=torch.int32, device=gc.DEV)
+    pk, pv = case.pool.k.clone(), case.pool.v.clone()
+    want_k, want_v = pk.clone(), pv.clone()
+    pkv.cache_write(kn, vn, pk, pv, case.block_table, sk - 1, cu)   # token b at position seqlens[b] - 1
+    pos = (sk - 1).long()
+    blk = case.block_table.long()[torch.arange(B, device=gc.DEV), pos // BS]
+    want_k[blk, pos % BS] = kn
+    want_v[blk, pos % BS] = vn
+    torch.cuda.synchronize()
+    assert torch.equal(pk.view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(pv.view(torch.int16), want_v.view(torch.int16))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("shape", [(16, 16, 4, 16, 5000), (24, 32, 8, 256, 6000), (40, 8, 2, 24, 3000)])
 def test_dispatch_orders_keep_bits(dtype, shape):
