@@ -1089,7 +1089,16 @@ __global__ __launch_bounds__(64, T::KVB == 1 ? 2 : 1) void decode2_kernel(AttnAr
   }
 }
 
-constexpr int kMergeWavesPerRow = 2;
+// Waves per (row, query head) of the merge.  One wave (two head-dim elements
+// per lane at d = 128) against two: the same time for 128 chunks per row
+// (long-context decode), and for rows of few chunks, where the merge is a
+// chain of dependent loads per wave and half the waves means fewer rounds of
+// them, 128 ragged sequences 0.3983 -> 0.3928 ms, 17-token chunked prefill
+// 17.35 -> 16.96 ms (in-process A/B, same bits; four waves were slower).
+#ifndef PKV_MERGE_WPR
+#define PKV_MERGE_WPR 1
+#endif
+constexpr int kMergeWavesPerRow = PKV_MERGE_WPR;
 // Chunks per round of the merge: two rounds in flight are 3 * 2 * PF loads,
 // which must stay within the 63 outstanding loads the wave's counter tracks
 // (with 16, the fold of one round waited for part of the next).  In-process
