@@ -267,8 +267,12 @@ Plan make_plan(const pkv_layout& l, bool append = false) {
   // repaid by uniform batches or long contexts (64 x 4096: +3.7%, 16 x
   // 131072: +0.4%).
   const int64_t jobs = static_cast<int64_t>(l.batch) * l.num_heads_k * p.maxc;
+  // Every sequence within one 1024-key chunk: a row's fold has one term, so
+  // the split kernels write out / lse themselves (the merge's operations on
+  // that term) -- no partials, no workspace, no merge launch.
+  p.lp.direct = !full && p.maxc == 1;
   p.lp.lpt = PKV_DECODE_LPT && !full && waves == 1 && l.dtype != PKV_F32 && p.cpi == 1 && p.maxc <= 16 &&
-             jobs > 2048 && jobs <= INT32_MAX;
+             jobs > 2048 && jobs <= INT32_MAX && !p.lp.direct;
   // One-wave bf16 decode: the two-stage kernel (two tiles in flight, 416
   // registers, one wave per SIMD; same bits) once the grid exceeds one round
   // of one-wave slots (256 CUs x 4 SIMDs).  In-process A/B against the
@@ -280,7 +284,7 @@ Plan make_plan(const pkv_layout& l, bool append = false) {
   p.lp.batch = l.batch;
   p.lp.hk = l.num_heads_k;
   p.lp.total_q = l.total_q;
-  if (full || l.total_q == 0 || p.maxc == 0) {
+  if (full || l.total_q == 0 || p.maxc == 0 || p.lp.direct) {
     p.ws_bytes = 0;
     p.lp.lpt = false;
   } else {
@@ -373,6 +377,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.job_pref = p.lp.lpt ? reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + p.off_jobs) : nullptr;
   a.nbatch = l->batch;
   a.nhk = l->num_heads_k;
+  a.direct = p.lp.direct ? 1 : 0;
   {
     // One-wave decode kernels: sequence-fastest dispatch for grids of at most
     // two rounds of wave slots whose (sequence, KV head) pairs span at least 4

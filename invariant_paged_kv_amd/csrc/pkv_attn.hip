@@ -53,6 +53,40 @@ __device__ __forceinline__ void store_out(void* out, int64_t elem, const f32x4 (
   }
 }
 
+// A row with a single chunk (AttnArgs::direct): the chunk result (mc, lc, oc)
+// folded into the empty row state and written, the same operations the merge
+// and the full path apply to a row whose keys lie in one chunk (mc = -inf, no
+// visible key: out = 0, lse = -inf).
+template <class T, int D>
+__device__ __forceinline__ void write_one_chunk(const AttnArgs& a, int64_t rh, float mc, float lc,
+                                                const f32x4 (&oc)[D / 16]) {
+  float M = -INFINITY, Ls = 0.f;
+  f32x4 O[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (mc != -INFINITY) {
+    const FoldCoef<T> f = fold_coef<T>(M, mc);
+    Ls = fold_val(Ls, f.a, lc, f.b);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[dt][i] = fold_val(O[dt][i], f.a, oc[dt][i], f.b);
+    M = f.mn;
+  }
+  if ((lane_id() >> 4) == 0) a.lse[rh] = final_lse<T>(M, Ls);
+  store_out<T, D>(a.out, rh * D, O, M, Ls, a.v_scale);
+}
+
+// The direct write of columns without a visible key (a column block whose
+// sequence has no key for any of its rows: no chunk to compute).
+template <class T, int D>
+__device__ __forceinline__ void write_empty_column(const AttnArgs& a, int64_t rh) {
+  f32x4 z[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) z[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  write_one_chunk<T, D>(a, rh, -INFINITY, 0.f, z);
+}
+
 #ifndef PKV_ATTN_XCD
 #define PKV_ATTN_XCD 1
 #endif
@@ -167,7 +201,16 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
   if constexpr (SPLIT) {
     c_begin = a.chunk0 + item * a.cpi;
     c_end = min(min(c_begin + a.cpi, nchunks), a.chunk1);
-    if (c_begin >= c_end) return;
+    if (c_begin >= c_end) {
+      if (a.direct && item == 0) {  // no visible key in the block: its rows still get out and lse
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int col = col0 + ((static_cast<int>(threadIdx.x) >> 6) * NT + nt) * 16 + (lane_id() & 15);
+          if (col < ncols) write_empty_column<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g);
+        }
+      }
+      return;
+    }
   }
 
   const Append ap = make_append<APPEND>(n, L, q0, col0 + COLS >= ncols);
@@ -326,7 +369,9 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
         const float lc = column_sum(st.l[nt]);
         if constexpr (SPLIT) {
           const int col = cols[nt];
-          if (col < ncols) {
+          if (col < ncols && a.direct) {
+            write_one_chunk<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g, st.m[nt], lc, st.o[nt]);
+          } else if (col < ncols) {
             const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.ps_row + c * a.ps_chunk;
             if (G == 0) {
               a.part_ml[2 * idx] = st.m[nt];
@@ -897,7 +942,13 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   const int nchunks = jmax > 0 ? (jmax + KC - 1) / KC : 0;
   const int c_begin = a.chunk0 + item * a.cpi;
   const int c_end = min(min(c_begin + a.cpi, nchunks), a.chunk1);
-  if (c_begin >= c_end) return;
+  if (c_begin >= c_end) {
+    if (a.direct && item == 0) {  // no visible key in the block: its rows still get out and lse
+      const int col = col0 + (lane_id() & 15);
+      if (col < ncols) write_empty_column<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g);
+    }
+    return;
+  }
   const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
   const Append ap = make_append<APPEND>(n, L, q0, col0 + 16 >= ncols);
 
@@ -957,7 +1008,9 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
       softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
     }
     const float lc = column_sum(st.l[0]);
-    if (col < ncols) {
+    if (col < ncols && a.direct) {
+      write_one_chunk<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g, st.m[0], lc, st.o[0]);
+    } else if (col < ncols) {
       const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.ps_row + c * a.ps_chunk;
       if (G == 0) {
         a.part_ml[2 * idx] = st.m[0];
@@ -1003,7 +1056,9 @@ __device__ __forceinline__ void decode2_tile(const AttnArgs& a, const int32_t* b
   softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
   if ((t + 1) % TPC == 0 || t + 1 == t_end) {
     const float lc = column_sum(st.l[0]);
-    if (col_ok) {
+    if (col_ok && a.direct) {
+      write_one_chunk<T, D>(a, part_row, st.m[0], lc, st.o[0]);
+    } else if (col_ok) {
       const int64_t idx = part_row * a.ps_row + static_cast<int64_t>(t / TPC) * a.ps_chunk;
       if ((lane_id() >> 4) == 0) {
         a.part_ml[2 * idx] = st.m[0];
@@ -1041,7 +1096,13 @@ __global__ __launch_bounds__(64, T::KVB == 1 ? 2 : 1) void decode2_kernel(AttnAr
   const int nchunks = jmax > 0 ? (jmax + KC - 1) / KC : 0;
   const int c_begin = a.chunk0 + item * a.cpi;
   const int c_end = min(min(c_begin + a.cpi, nchunks), a.chunk1);
-  if (c_begin >= c_end) return;
+  if (c_begin >= c_end) {
+    if (a.direct && item == 0) {  // no visible key in the block: its rows still get out and lse
+      const int col = col0 + (lane_id() & 15);
+      if (col < ncols) write_empty_column<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g);
+    }
+    return;
+  }
   const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
   const Append ap = make_append<APPEND>(n, L, q0, col0 + 16 >= ncols);
 
@@ -1272,7 +1333,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
     hipLaunchKernelGGL((attn_kernel<T, D, 4, kSplitGroups, true, APPEND, false>), grid, dim3(256), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.skip_merge) return e;
+  if (e != hipSuccess || pl.skip_merge || pl.direct) return e;
   MergeArgs m;
   m.cu_q = a.cu_q;
   m.seqlens_k = a.seqlens_k;

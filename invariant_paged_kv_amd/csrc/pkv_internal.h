@@ -56,6 +56,10 @@ struct AttnArgs {
   // One-wave decode kernels, plain grid: dispatch order of the work items
   // (0: items of one (sequence, KV head) consecutive; 1: sequence fastest).
   int32_t dorder;
+  // Split kernels: every column's visible keys lie in chunk 0 (at most 1024
+  // keys per sequence), so a row's fold has a single term; the kernels write
+  // out / lse themselves instead of partials, and no merge is launched.
+  int32_t direct;
 };
 
 struct MergeArgs {
@@ -87,6 +91,7 @@ struct LaunchPlan {
   bool two_stage;  // split path, one-wave bf16 kernel: two tiles in flight (decode2_kernel)
   bool append;     // fused append of k_new / v_new
   bool skip_merge; // split path: write the chunk partials only
+  bool direct;     // split path: out / lse written by the split kernels (AttnArgs::direct), no merge
   int waves;       // split path: waves per work group (1 or 4)
   int items;       // split path: work items per column block along the keys
   int batch, hk;

@@ -188,6 +188,17 @@ def test_chunk_partials_and_merge_reject_bad_arguments():
     assert L.pkv_attn_merge_partials(96, 104, 4, ctypes.byref(lay), 64, 64, 1, 48, 64, None) == -4
 
 
+def test_single_chunk_decode_needs_no_workspace():
+    """Sequences within one 1024-key chunk: the split kernels write out / lse themselves (no partials,
+    no merge), so the split path asks for no workspace; from 1025 keys on it does."""
+    L = pkv.lib()
+    one = good_layout(max_blocks_per_seq=64)      # 64 x 16 = 1024 keys
+    assert L.pkv_attn_workspace_size(ctypes.byref(one)) == 0
+    two = good_layout(max_blocks_per_seq=64, max_seqlen_k=1025, num_blocks=256)
+    two.max_blocks_per_seq = 65
+    assert L.pkv_attn_workspace_size(ctypes.byref(two)) > 0
+
+
 def test_noalloc_rejects_a_split_path_beyond_the_scratch_before_any_device_call():
     """The size check of pkv_attn_forward_noalloc runs on the host first: on a
     machine without a GPU it still answers PKV_ERR_WORKSPACE (a device call
@@ -202,7 +213,7 @@ def test_noalloc_rejects_a_split_path_beyond_the_scratch_before_any_device_call(
     assert rc == pkv.PKV_ERR_WORKSPACE
     assert b"scratch" in L.pkv_last_error()
     # a layout that fits passes the size check; a NULL q is then reported, still before any device call
-    small = good_layout()
+    small = good_layout(max_blocks_per_seq=128)   # 2048 keys: two chunks, partials in the scratch
     assert 0 < L.pkv_attn_workspace_size(ctypes.byref(small)) <= pkv.NOALLOC_MAX_BYTES
     assert L.pkv_attn_forward_noalloc(None, 32, 48, ctypes.byref(small), 64, 64, 64, 1, 0.1, 80, 96,
                                       None) == pkv.PKV_ERR_NULL
