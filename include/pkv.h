@@ -150,8 +150,9 @@ typedef struct pkv_layout {
  * positions finite.  A row with no
  * visible key (e.g. seqlens_k[b] = 0, or a causal row at position < 0 when
  * seqlens_k[b] is below the row count) gets out = 0 and lse = -inf.  The split (decode)
- * path needs a workspace; this entry point takes it from the stream-ordered
- * allocator (hipMallocAsync / hipFreeAsync on `stream`).
+ * path needs a workspace for keys beyond one 1024-key chunk (max_seqlen_k above
+ * 1024); this entry point takes it from the stream-ordered allocator
+ * (hipMallocAsync / hipFreeAsync on `stream`).
  * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (also softmax_scale <= 0 or not finite),
  * PKV_ERR_DTYPE, PKV_ERR_ALIGN (q, caches,
  * out must be 16-byte aligned and every stride a multiple of 16 bytes),
@@ -217,7 +218,10 @@ int pkv_attn_forward_append(const void* q, const void* k_new, const void* v_new,
                             const int32_t* cu_seqlens_q, int causal, float softmax_scale, void* out, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes the split path needs for this layout (0 if it is never used):
+/* Workspace bytes the split path needs for this layout (0 if it is never used,
+ * and 0 when every sequence lies within one 1024-key chunk -- max_seqlen_k, or
+ * max_blocks_per_seq * block_size when it is 0, at most 1024 -- where the split
+ * kernels write out / lse themselves and no merge runs):
  * the fp32 chunk partials (total_q * Hq * chunks * (d + 2) floats) and, when
  * the one-wave bf16/FP8 decode kernels take a longest-first job list (at most
  * 16 chunks of keys and more than 2048 (sequence, KV head, chunk) slots),
