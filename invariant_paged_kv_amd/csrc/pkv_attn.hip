@@ -914,21 +914,48 @@ __global__ __launch_bounds__(64 * W, 2) void prefill_kernel(AttnArgs a) {
 
 // Two waves per SIMD (<= 256 registers): 8 waves per CU, each with one tile
 // (32 KiB at d = 128) of K/V loads in flight while it computes the previous one.
-template <class T, int D, bool APPEND, bool U>
-__global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
+//
+// NW > 1: the work group is one (sequence, KV head, column block) and wave w
+// computes chunk w (sequences of at most NW chunks).  The waves leave their
+// chunk results (m, l, o of 16 columns) in LDS instead of HBM, and after one
+// barrier the work group folds them in ascending chunk order and writes out /
+// lse: the merge's operations on the same values (chunks past a column's own
+// limit hold m = -inf and are skipped, as the merge never reaches them), so
+// the same bits, without the partials' HBM round trip or the merge launch.
+// Used with NW = 2: one round of 2-chunk decode, 64 x 2048 keys (Hq 16 / Hkv
+// 4) 0.0593 -> 0.0564 ms, 32 x 2048 (32 / 8) 0.0592 -> 0.0562.  With 4 chunks
+// per group the 64 x 4096 shard went 0.1003 -> 0.1056 ms (the one-wave kernels'
+// order puts the 4 KV heads of one chunk on one CU, reading the same DRAM rows
+// together; a group holds one KV head's chunks instead), and with 8 (16 x 8192,
+// Hq 64 / Hkv 8: 128 groups) half the CUs idled, 0.1051 -> 0.1358 ms.
+template <class T, int D, bool APPEND, bool U, int NW = 1>
+__global__ __launch_bounds__(64 * NW, NW == 1 ? 2 : 1) void decode_kernel(AttnArgs a) {
   if (dbg_skip(a.dbg_word)) return;
   using G_ = TileGeom<T, D>;
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[G_::VBYTES];
+  static_assert(NW == 1 || !APPEND, "the in-group fold is not combined with the fused append");
+  static_assert(NW == 1 || 16 * (D + 2) * 4 <= G_::VBYTES, "a wave's chunk result fits its V area");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NW * G_::VBYTES];
+  // the wave index is the same in every lane: say so, so that the chunk range,
+  // the loop bounds and the block ids derived from it stay scalar
+  const int wave_u = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  unsigned char* const v_lds = lds + wave_u * G_::VBYTES;
 
   // Consecutive work groups take consecutive chunks of one (sequence, KV
   // head): concurrently running waves then read different cache blocks
   // (ordering the KV heads of one chunk next to each other measured ~9%
   // slower on the long-context workload).
   int b, hk, cb, item;
-  decode_item(a, b, hk, cb, item);
-  if (a.job_pref) {  // longest-first job list (one column block, one chunk per item)
-    cb = 0;
-    if (!decode_job(a, blockIdx.x, b, hk, item)) return;
+  if constexpr (NW > 1) {
+    cb = blockIdx.x;
+    hk = blockIdx.y;
+    b = blockIdx.z;
+    item = wave_u;
+  } else {
+    decode_item(a, b, hk, cb, item);
+    if (a.job_pref) {  // longest-first job list (one column block, one chunk per item)
+      cb = 0;
+      if (!decode_job(a, blockIdx.x, b, hk, item)) return;
+    }
   }
   const int n = a.seqlens_k[b];
   const int q0 = a.cu_q[b];
@@ -942,83 +969,133 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(AttnArgs a) {
   const int nchunks = jmax > 0 ? (jmax + KC - 1) / KC : 0;
   const int c_begin = a.chunk0 + item * a.cpi;
   const int c_end = min(min(c_begin + a.cpi, nchunks), a.chunk1);
-  if (c_begin >= c_end) {
-    if (a.direct && item == 0) {  // no visible key in the block: its rows still get out and lse
-      const int col = col0 + (lane_id() & 15);
-      if (col < ncols) write_empty_column<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g);
-    }
-    return;
-  }
-  const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
-  const Append ap = make_append<APPEND>(n, L, q0, col0 + 16 >= ncols);
-
-  const int lane = lane_id();
-  const int G = lane >> 4;
-  const int col = col0 + (lane & 15);
-  const int lim[1] = {column_limit(col, ncols, g, n, L, a.causal)};
-  QOps<T, D> q;
-  if (col < ncols) {
-    const int64_t qelem = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * D;
-    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB;
-#pragma unroll
-    for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + qk_piece_off<T>(k, G));
-  } else {
-#pragma unroll
-    for (int k = 0; k < G_::NK; ++k) q.v[k] = u32x4{0, 0, 0, 0};
-  }
-
-  const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
-  if constexpr (APPEND) {
-    if (ap.writer) append_rows<T, D>(a, bt, hk, max(ap.n_old, c_begin * KC), jlast, ap);
-  }
-  int j0 = c_begin * KC;
-  int ids[KT / 16];
-  TileRegs<T, D> r;
-  tile_block_ids<U>(a, bt, j0, jlast, ids);
-  // V then K, the order the loop issues them in (see below)
-  tile_load_regs<T, D, APPEND, U>(a, hk, j0, jlast, ids, r, false, true, ap);
-  __builtin_amdgcn_sched_barrier(0);
-  tile_load_regs<T, D, APPEND, U>(a, hk, j0, jlast, ids, r, true, false, ap);
-  tile_block_ids<U>(a, bt, j0 + KT, jlast, ids);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // Per tile: copy V(t) to LDS and refill those registers with V(t+1); QK on
-  // K(t) and refill with K(t+1); then softmax + PV(t) while t+1 is in flight.
-  ChunkState<D, 1> st;
-  for (int c = c_begin; c < c_end; ++c) {
-    chunk_reset(st);
-    const int jend = min((c + 1) * KC, jmax);
-    for (; j0 < jend; j0 += KT) {
-      // The next tile's loads are issued unconditionally: past the item's
-      // last key every row clamps to row jlast - 1 (a cache hit), and a load
-      // under a branch would make the compiler wait for all loads in flight
-      // where the branch rejoins.
-      const int jn = j0 + KT;
-      tile_edge<T, D>(j0, jlast, r);
-      tile_store_v<T, D>(v_lds, r);
-      tile_load_regs<T, D, APPEND, U>(a, hk, jn, jlast, ids, r, false, true, ap);
-      // Loads complete in issue order: keep all of V(t+1) ahead of K(t+1), so
-      // waiting for V(t+1) at the next tile leaves K(t+1) in flight.
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 s[1][KT / 16];
-      qk_tile_regs<T, D>(r, q, s[0]);
-      tile_load_regs<T, D, APPEND, U>(a, hk, jn, jlast, ids, r, true, false, ap);
-      tile_block_ids<U>(a, bt, jn + KT, jlast, ids);
-      __builtin_amdgcn_sched_barrier(0);
-      softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
-    }
-    const float lc = column_sum(st.l[0]);
-    if (col < ncols && a.direct) {
-      write_one_chunk<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g, st.m[0], lc, st.o[0]);
-    } else if (col < ncols) {
-      const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.ps_row + c * a.ps_chunk;
-      if (G == 0) {
-        a.part_ml[2 * idx] = st.m[0];
-        a.part_ml[2 * idx + 1] = lc;
+  const bool has = c_begin < c_end;  // NW > 1: a wave past the sequence's last chunk only joins the fold
+  if (!has) {
+    if constexpr (NW == 1) {
+      if (a.direct && item == 0) {  // no visible key in the block: its rows still get out and lse
+        const int col = col0 + (lane_id() & 15);
+        if (col < ncols) write_empty_column<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g);
       }
-      float* po = a.part_o + idx * D;
+      return;
+    }
+  }
+  if (has) {
+    const int jlast = min(c_end * KC, jmax);   // keys this item reads: [c_begin*KC, jlast)
+    const Append ap = make_append<APPEND>(n, L, q0, col0 + 16 >= ncols);
+
+    const int lane = lane_id();
+    const int G = lane >> 4;
+    const int col = col0 + (lane & 15);
+    const int lim[1] = {column_limit(col, ncols, g, n, L, a.causal)};
+    QOps<T, D> q;
+    if (col < ncols) {
+      const int64_t qelem = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * D;
+      const unsigned char* qp = static_cast<const unsigned char*>(a.q) + qelem * T::EB;
+  #pragma unroll
+      for (int k = 0; k < G_::NK; ++k) q.v[k] = *reinterpret_cast<const u32x4*>(qp + qk_piece_off<T>(k, G));
+    } else {
+  #pragma unroll
+      for (int k = 0; k < G_::NK; ++k) q.v[k] = u32x4{0, 0, 0, 0};
+    }
+
+    const int32_t* bt = a.block_table + (int64_t)b * a.mbps;
+    if constexpr (APPEND) {
+      if (ap.writer) append_rows<T, D>(a, bt, hk, max(ap.n_old, c_begin * KC), jlast, ap);
+    }
+    int j0 = c_begin * KC;
+    int ids[KT / 16];
+    TileRegs<T, D> r;
+    tile_block_ids<U>(a, bt, j0, jlast, ids);
+    // V then K, the order the loop issues them in (see below)
+    tile_load_regs<T, D, APPEND, U>(a, hk, j0, jlast, ids, r, false, true, ap);
+    __builtin_amdgcn_sched_barrier(0);
+    tile_load_regs<T, D, APPEND, U>(a, hk, j0, jlast, ids, r, true, false, ap);
+    tile_block_ids<U>(a, bt, j0 + KT, jlast, ids);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Per tile: copy V(t) to LDS and refill those registers with V(t+1); QK on
+    // K(t) and refill with K(t+1); then softmax + PV(t) while t+1 is in flight.
+    ChunkState<D, 1> st;
+    for (int c = c_begin; c < c_end; ++c) {
+      chunk_reset(st);
+      const int jend = min((c + 1) * KC, jmax);
+      for (; j0 < jend; j0 += KT) {
+        // The next tile's loads are issued unconditionally: past the item's
+        // last key every row clamps to row jlast - 1 (a cache hit), and a load
+        // under a branch would make the compiler wait for all loads in flight
+        // where the branch rejoins.
+        const int jn = j0 + KT;
+        tile_edge<T, D>(j0, jlast, r);
+        tile_store_v<T, D>(v_lds, r);
+        tile_load_regs<T, D, APPEND, U>(a, hk, jn, jlast, ids, r, false, true, ap);
+        // Loads complete in issue order: keep all of V(t+1) ahead of K(t+1), so
+        // waiting for V(t+1) at the next tile leaves K(t+1) in flight.
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 s[1][KT / 16];
+        qk_tile_regs<T, D>(r, q, s[0]);
+        tile_load_regs<T, D, APPEND, U>(a, hk, jn, jlast, ids, r, true, false, ap);
+        tile_block_ids<U>(a, bt, jn + KT, jlast, ids);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax_pv_tile<T, D, 1, true, false>(st, s, lim, j0, a.mul, v_lds);
+      }
+      const float lc = column_sum(st.l[0]);
+      if constexpr (NW > 1) {  // this wave's chunk result into its V area, for the fold below
+        float* pc = reinterpret_cast<float*>(v_lds) + (lane & 15) * (D + 2);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * G) = st.o[0][dt];
+        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(pc + 16 * dt + 4 * G) = st.o[0][dt];
+        if (G == 0) {
+          pc[D] = st.m[0];
+          pc[D + 1] = lc;
+        }
+      } else if (col < ncols && a.direct) {
+        write_one_chunk<T, D>(a, (int64_t)(q0 + col / g) * a.hq + hk * g + col % g, st.m[0], lc, st.o[0]);
+      } else if (col < ncols) {
+        const int64_t idx = ((int64_t)(q0 + col / g) * a.hq + hk * g + col % g) * a.ps_row + c * a.ps_chunk;
+        if (G == 0) {
+          a.part_ml[2 * idx] = st.m[0];
+          a.part_ml[2 * idx + 1] = lc;
+        }
+        float* po = a.part_o + idx * D;
+  #pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * G) = st.o[0][dt];
+      }
+    }
+  }
+  if constexpr (NW > 1) {
+    // every wave's chunk result is in LDS (16 columns x (d values, m, l)); fold
+    // them per column in ascending chunk order, each thread D / TPC elements
+    __syncthreads();
+    constexpr int TPC = 64 * NW / 16;  // threads per column
+    constexpr int EPT = D / TPC;       // head-dim elements per thread
+    static_assert(EPT * TPC == D, "columns split evenly over the work group");
+    const int t = threadIdx.x;
+    const int cl = t / TPC, e0 = (t % TPC) * EPT;
+    float M = -INFINITY, Ls = 0.f;
+    float O[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) O[e] = 0.f;
+    for (int c = 0; c < min(nchunks, NW); ++c) {
+      const float* pc = reinterpret_cast<const float*>(lds + c * G_::VBYTES) + cl * (D + 2);
+      const float mc = pc[D];
+      if (mc == -INFINITY) continue;
+      const FoldCoef<T> f = fold_coef<T>(M, mc);
+      Ls = fold_val(Ls, f.a, pc[D + 1], f.b);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) O[e] = fold_val(O[e], f.a, pc[e0 + e], f.b);
+      M = f.mn;
+    }
+    const int col = col0 + cl;
+    if (col < ncols) {
+      const int64_t rh = (int64_t)(q0 + col / g) * a.hq + hk * g + col % g;
+      if (t % TPC == 0) a.lse[rh] = final_lse<T>(M, Ls);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const float v = final_val(M, O[e], Ls, a.v_scale);
+        if constexpr (T::EB == 2)
+          static_cast<uint16_t*>(a.out)[rh * D + e0 + e] = static_cast<uint16_t>(bf16_rne_bits(v));
+        else
+          static_cast<float*>(a.out)[rh * D + e0 + e] = v;
+      }
     }
   }
 }
@@ -1292,6 +1369,16 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
     return hipGetLastError();
   }
   dim3 grid(a.ncb * pl.items, pl.hk, pl.batch);
+  if constexpr (T::EB == 2 && T::KVB == 2 && !APPEND) {
+    if (pl.fold_waves == 2) {  // one work group per (sequence, KV head, column block), a wave per chunk
+      const dim3 fgrid(a.ncb, pl.hk, pl.batch);
+      if (uni)
+        hipLaunchKernelGGL((decode_kernel<T, D, false, true, 2>), fgrid, dim3(128), 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_kernel<T, D, false, false, 2>), fgrid, dim3(128), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (pl.lpt) {
     // prefix counts of the longest-first job list, then one work item per job slot
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.seqlens_k, a.cu_q, pl.batch,
@@ -1333,7 +1420,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, const LaunchPlan& pl, hipStre
     hipLaunchKernelGGL((attn_kernel<T, D, 4, kSplitGroups, true, APPEND, false>), grid, dim3(256), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.skip_merge || pl.direct) return e;
+  if (e != hipSuccess || pl.skip_merge || pl.direct || pl.fold_waves) return e;
   MergeArgs m;
   m.cu_q = a.cu_q;
   m.seqlens_k = a.seqlens_k;

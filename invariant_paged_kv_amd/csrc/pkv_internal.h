@@ -92,6 +92,7 @@ struct LaunchPlan {
   bool append;     // fused append of k_new / v_new
   bool skip_merge; // split path: write the chunk partials only
   bool direct;     // split path: out / lse written by the split kernels (AttnArgs::direct), no merge
+  int fold_waves;  // split path, one-wave bf16 kernel: 0, or waves per work group folding its chunks (no merge)
   int waves;       // split path: waves per work group (1 or 4)
   int items;       // split path: work items per column block along the keys
   int batch, hk;
