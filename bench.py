@@ -225,7 +225,7 @@ def main():
     settle(torch, rescore)
     ev0.record(stream)
     for _ in range(5):
-        rescore()
+        rs_out, rs_lse = rescore()
     ev1.record(stream)
     ev1.synchronize()
     rs_ms = ev0.elapsed_time(ev1) / 5
@@ -234,14 +234,20 @@ def main():
                                  "ms": round(rs_ms, 3), "tflops": round(rs_flops / (rs_ms * 1e-3) / 1e12, 2),
                                  "frac": round(rs_flops / (rs_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                  "flops": rs_flops}
-    del q_rs
+    if not args.no_cpu_baseline:
+        # the last row and the first of each of four sequences' 64 re-scored rows
+        picks = [(b, b * RS + r, N - RS + r) for b in (0, 5, 10, 15) for r in (RS - 1, 0)]
+        result["rescore_prefill"]["oracle"] = oracle_rows(torch, pool, bt, q_rs, picks, HQ, HK, D, BS, scale,
+                                                          rs_out, rs_lse)
+    del q_rs, rs_out, rs_lse
 
     if not args.no_configs:
         result["decode_configs"] = bench_decode_configs(torch, pkv, gen, want_cpu=not args.no_cpu_baseline)
     if not args.no_fp8:
         result["fp8_decode"] = bench_fp8_decode(torch, pkv, gen, B, N, args.steps, args.warmup, attn_avg_ms)
     if not args.no_prefill:
-        result["prefill"], result["backward"], chunked = bench_prefill(torch, pkv, gen)
+        result["prefill"], result["backward"], chunked = bench_prefill(torch, pkv, gen,
+                                                                       want_cpu=not args.no_cpu_baseline)
         result["chunked_prefill"] = chunked
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["oracle_parity"] = cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale,
@@ -560,7 +566,7 @@ def bench_fp8_decode(torch, pkv, gen, B, N, steps, warmup, bf16_ms):
             "speedup_vs_bf16_call": round(bf16_ms / ms, 3), "bitwise_decode_eq_prefill_kernel": same}
 
 
-def bench_prefill(torch, pkv, gen, reps: int = 5):
+def bench_prefill(torch, pkv, gen, reps: int = 5, want_cpu: bool = True):
     """Full causal prefill, batch 8 x 8192 tokens, Hq 16, Hkv 4, d 128, bs 16 (TFLOP/s of causal pairs)."""
     dev = "cuda"
     B, HQ, HK, D, BS, S = 8, 16, 4, 128, 16, 8192
@@ -590,17 +596,22 @@ def bench_prefill(torch, pkv, gen, reps: int = 5):
     fwd = {"workload": "full causal prefill batch 8 x 8192, Hq 16, Hkv 4, d 128, bs 16",
            "ms": round(ms, 3), "tflops": round(tf, 2), "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": flops}
+    if want_cpu:
+        # rows spread over the causal range of every sequence, longest first
+        out, lse = call()
+        picks = [(b, b * S + p, p) for p in range(S - 1, 0, -256) for b in range(B)]
+        fwd["oracle"] = oracle_rows(torch, pool, bt, q, picks, HQ, HK, D, BS, scale, out, lse)
 
     # Backward of the same prefill: dq, dk, dv for a seeded N(0,1) cotangent.
     # Algorithmic FLOPs: the five products dP, dV, dK, dQ and the recomputed S
     # over the causal pairs, 2.5x the forward's two.
     out, lse = call()
     chunked = []
-    for c in (17, 1024):
+    for c, fused in ((17, False), (17, True), (1024, False)):
         try:
-            chunked.append(bench_chunked_prefill(torch, pkv, pool, bt, q, out, lse, S, scale, c))
+            chunked.append(bench_chunked_prefill(torch, pkv, pool, bt, q, out, lse, S, scale, c, fused=fused))
         except (RuntimeError, ValueError) as exc:   # reported in the line; the other figures still print
-            chunked.append({"chunk_tokens": c, "error": str(exc)[:200]})
+            chunked.append({"chunk_tokens": c, "fused": fused, "error": str(exc)[:200]})
     dout = gen.randn((B * S, HQ, D), "bf16", generator=g, device=dev)
     cuk = torch.arange(0, B * S + 1, S, dtype=torch.int32, device=dev)
     dq = torch.empty_like(q)
@@ -716,9 +727,10 @@ def bench_chunked_prefill(torch, pkv, pool, bt, q, ref_out, ref_lse, S, scale, c
     timed_same = same_as_one_shot()
     flops = 4.0 * D * HQ * B * (S * (S + 1) / 2)
     kv_bytes = sum(B * c["hi"] * HK * D * 2 * 2 for c in calls)   # every call re-reads the keys it sees
+    per_call = "pkv_attn_forward_append" if fused else "cache_write + attention"
     res = {"workload": f"the same prefill in {len(calls)} chunks of {chunk} tokens per sequence "
-                       "(cache_write + attention per chunk, replayed as one HIP graph)",
-           "chunk_tokens": chunk, "calls": len(calls), "ms": round(ms, 3),
+                       f"({per_call} per chunk, replayed as one HIP graph)",
+           "chunk_tokens": chunk, "fused": fused, "calls": len(calls), "ms": round(ms, 3),
            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "kv_reread_bytes": kv_bytes, "kv_GBs": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
@@ -769,6 +781,46 @@ def cpu_baseline(torch, gen, pool, bt, q, N, HK, D, BS, scale, out, lse, budget_
             "sample": f"{seqs} of {B} sequences of one decode step (all {HQ} heads, {N} keys each), "
                       f"{spent:.1f} s"}, {"out_max_abs": err_o, "lse_max_abs": err_l, "sequences": seqs,
                                            "tolerance": {"out": 2e-2, "lse": 1e-3}}
+
+
+def oracle_rows(torch, pool, bt, q, picks, HQ, HK, D, BS, scale, out, lse, budget_s: float = 4.0):
+    """The float64 oracle on sampled causal rows of a prefill, timed on the host.
+
+    ``picks`` lists (sequence, row of q, key position p): each row is the
+    oracle's one-row call over that sequence's keys 0..p (a causal row at
+    position p sees exactly those), taken in order until ``budget_s`` of host
+    time is spent.  Returns the oracle's TFLOP/s (4 * d * Hq * (p + 1) per row)
+    and its max-abs agreement with the GPU's out / lse of those rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    gout = out.double().cpu().numpy()
+    glse = lse.double().cpu().numpy()
+    row = HK * D
+    lay = oracle.Layout("bf16", HQ, HK, D, BS, 0, (BS * row, row, D), 0, (BS * row, row, D))
+    spent, flops, rows, eo, el = 0.0, 0.0, 0, 0.0, 0.0
+    for b, r, p in picks:
+        n = p + 1
+        nblk = math.ceil(n / BS)
+        ids = bt[b, :nblk].long()
+        kf = pool.k.index_select(0, ids).cpu().contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+        vf = pool.v.index_select(0, ids).cpu().contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+        qh = q[r:r + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oo, ol = oracle.attention(qh, kf, vf, lay, np.arange(nblk, dtype=np.int32)[None, :], [n], [0, 1], True, scale)
+        spent += time.perf_counter() - t0
+        eo = max(eo, float(np.max(np.abs(gout[r] - oo[0]))))
+        el = max(el, float(np.max(np.abs(glse[r] - ol[0]))))
+        flops += 4.0 * D * HQ * n
+        rows += 1
+        if spent >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {len(picks)} sampled rows, all {HQ} heads ({spent:.1f} s)",
+            "out_max_abs": eo, "lse_max_abs": el, "tolerance": {"out": 2e-2, "lse": 1e-3}}
 
 
 if __name__ == "__main__":
