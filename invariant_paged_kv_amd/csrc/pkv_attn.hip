@@ -123,6 +123,9 @@ __device__ __forceinline__ void write_empty_column(const AttnArgs& a, int64_t rh
 #ifndef PKV_SPLIT_QK_ILP
 #define PKV_SPLIT_QK_ILP 1
 #endif
+#ifndef PKV_SPLIT_LOADERS
+#define PKV_SPLIT_LOADERS 1
+#endif
 
 template <class T, int D, int W, int NT, bool SPLIT, bool APPEND, bool U>
 __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a) {
@@ -160,6 +163,15 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
   // are those of the unstaggered kernel.
   constexpr bool kStagger = kLateCommit && NT == 1 && W == 8 && PKV_SPLIT_STAGGER != 0;
   constexpr int kBufs = kStagger ? 3 : (kDouble ? 2 : 1);
+  // Staggered split kernel whose column block leaves the last two waves
+  // without a column (at most 16 * (W - 2) columns, e.g. 17 rows x 4 heads):
+  // those two waves load and stage every tile in a loop of their own, and the
+  // waves with columns issue no tile loads or LDS tile writes -- the staging
+  // leaves their per-tile chain.  The same bytes reach the same LDS tiles
+  // between the same barriers, so no bit changes.  Not with the fused append
+  // (measured slower there: 16.90 -> 17.12 ms on 17-token chunks, where the
+  // plain call went 17.14 -> 15.82 ms).
+  constexpr bool kLoaders = kStagger && !APPEND && PKV_SPLIT_LOADERS != 0;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kBufs * G_::BYTES];
   unsigned char* k_lds = lds;
   unsigned char* v_lds = lds + G_::KBYTES;
@@ -240,6 +252,7 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
   // sequence) skips the arithmetic; its lanes still load their share of every
   // tile.  Wave-uniform, so barriers and loads stay the same for all waves.
   const bool live = __builtin_amdgcn_readfirstlane(col0 + wave * NT * 16 < ncols ? 1 : 0) != 0;
+  const bool lmode = kLoaders && ncols - col0 <= 16 * (W - 2);   // the same in every wave
   float M[NT], Ls[NT];
   f32x4 O[NT][D / 16];
   if constexpr (!SPLIT) {
@@ -264,15 +277,47 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
     // loads, measured 1.7% slower with it)
     constexpr bool kIds = kPrefetch && U && SPLIT && PKV_IDS_AHEAD;
     const int jb = c_begin * KC;
+    if constexpr (kLoaders) {
+      if (lmode && wave >= W - 2) {
+        // Loader waves: the tile schedule of the waves below (tile jb into
+        // buffer 0 first; after the barrier that starts tile t, tile t + 1
+        // from the register stage into buffer (t + 1) % 3, then tile t + 2's
+        // loads into the stage), each thread with a quarter of the tile.
+        const int ltid = static_cast<int>(threadIdx.x) - 64 * (W - 2);
+        TileStage<T, D, 2> lstg;
+        TileIds lids;
+        auto lissue = [&](int j) {
+          tile_issue<T, D, 2, APPEND, U, kIds>(a, bt, hk, j, jmax, lstg, ap, lids, ltid);
+          if constexpr (kIds) tile_ids_fetch<T, D, 2, U>(a, bt, j + KT, jmax, lids, ltid);
+        };
+        if constexpr (kIds) tile_ids_fetch<T, D, 2, U>(a, bt, jb, jmax, lids, ltid);
+        lissue(jb);
+        tile_commit<T, D, 2, APPEND>(a, bt, hk, jb, jmax, lstg, lds, lds + G_::KBYTES, ap, ltid);
+        lissue(jb + KT);
+        for (int c = c_begin; c < c_end; ++c) {
+          const int jend = min((c + 1) * KC, jmax);
+          for (int j0 = c * KC; j0 < jend; j0 += KT) {
+            __syncthreads();
+            unsigned char* const nk = lds + (((j0 - jb) / KT + 1) % 3) * G_::BYTES;
+            tile_commit<T, D, 2, APPEND>(a, bt, hk, j0 + KT, jmax, lstg, nk, nk + G_::KBYTES, ap, ltid);
+            lissue(j0 + 2 * KT);
+          }
+        }
+        return;  // no column: nothing to write
+      }
+    }
     auto issue = [&](int j, TileStage<T, D, W>& into) {
+      if (kLoaders && lmode) return;  // the loader waves stage the tiles
       tile_issue<T, D, W, APPEND, U, kIds>(a, bt, hk, j, jmax, into, ap, ids);
       if constexpr (kIds) tile_ids_fetch<T, D, W, U>(a, bt, j + KT, jmax, ids);
     };
-    if constexpr (kIds) tile_ids_fetch<T, D, W, U>(a, bt, jb, jmax, ids);
+    if constexpr (kIds) {
+      if (!(kLoaders && lmode)) tile_ids_fetch<T, D, W, U>(a, bt, jb, jmax, ids);
+    }
     if constexpr (kPrefetch) issue(jb, stg);
     if constexpr (kDouble) {
       // first tile into buffer 0, the second one's loads in flight
-      tile_commit<T, D, W, APPEND>(a, bt, hk, jb, jmax, stg, k_lds, v_lds, ap);
+      if (!(kLoaders && lmode)) tile_commit<T, D, W, APPEND>(a, bt, hk, jb, jmax, stg, k_lds, v_lds, ap);
       issue(jb + KT, stg);
     }
     ChunkState<D, NT> st;
@@ -319,7 +364,7 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? 1 : 2) void attn_kernel(AttnArgs a
         if constexpr (kPrefetch) {
           if constexpr (kLateCommit) {
             unsigned char* const nk = lds + (kStagger ? ((j0 - jb) / KT + 1) % 3 : ((j0 / KT) & 1) ^ 1) * G_::BYTES;
-            tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, ready, nk, nk + G_::KBYTES, ap);
+            if (!(kLoaders && lmode)) tile_commit<T, D, W, APPEND>(a, bt, hk, j0 + KT, jmax, ready, nk, nk + G_::KBYTES, ap);
           }
           issue(jn, ready);
         }

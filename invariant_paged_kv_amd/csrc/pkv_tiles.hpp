@@ -179,22 +179,29 @@ struct TileIds {
   uint32_t v = 0;
 };
 
+// `tid` (tile_ids_fetch, tile_issue, tile_commit): the thread's index among
+// the 64 * W threads that share the tile's pieces (default: threadIdx.x, the
+// whole work group; a subset of the waves passes its own numbering).
 template <class T, int D, int W, bool U>
-__device__ __forceinline__ void tile_ids_fetch(const AttnArgs& a, const int32_t* bt, int j0, int jmax, TileIds& ids) {
+__device__ __forceinline__ void tile_ids_fetch(const AttnArgs& a, const int32_t* bt, int j0, int jmax, TileIds& ids,
+                                               int tid = -1) {
   if constexpr (U) {
     using G_ = TileGeom<T, D>;
     constexpr int PER = TileStage<T, D, W>::PER;
+    const int t = tid < 0 ? static_cast<int>(threadIdx.x) : tid;
     const int i = min(lane_id(), PER - 1);
-    const int g0 = ((static_cast<int>(threadIdx.x) & ~63) + i * 64 * W) / G_::CPR & ~15;
+    const int g0 = ((t & ~63) + i * 64 * W) / G_::CPR & ~15;
     ids.v = static_cast<uint32_t>(bt[div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift)]);
   }
 }
 
 template <class T, int D, int W, bool APPEND, bool U, bool kFetched = false>
 __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
-                                           TileStage<T, D, W>& stg, const Append& ap, const TileIds& ids = {}) {
+                                           TileStage<T, D, W>& stg, const Append& ap, const TileIds& ids = {},
+                                           int tid = -1) {
   using G_ = TileGeom<T, D>;
   constexpr int PER = TileStage<T, D, W>::PER;
+  const int t = tid < 0 ? static_cast<int>(threadIdx.x) : tid;
   const unsigned char* kb = static_cast<const unsigned char*>(a.k);
   const unsigned char* vb = static_cast<const unsigned char*>(a.v);
   uint32_t ublk[PER];  // U: block ids of the wave's row groups (see load_tile)
@@ -205,7 +212,7 @@ __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt,
     auto per_group = [&] {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int row = (threadIdx.x + i * 64 * W) / G_::CPR;
+        const int row = (t + i * 64 * W) / G_::CPR;
         const int g0 = __builtin_amdgcn_readfirstlane(row) & ~15;
         const int bi = div_block(min(j0 + g0, jmax - 1), a.bs_mul, a.bs_shift);
         if constexpr (kFetched)
@@ -252,7 +259,7 @@ __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt,
   const unsigned char* const vbh = vb + (int64_t)hk * a.vhs * T::KVB;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int qi = threadIdx.x + i * 64 * W;
+    const int qi = t + i * 64 * W;
     const int row = qi / G_::CPR, part = qi % G_::CPR;
     const int jc = min(j0 + row, jmax - 1);
     const int off = kKvPiece<T> * part;
@@ -278,15 +285,16 @@ __device__ __forceinline__ void tile_issue(const AttnArgs& a, const int32_t* bt,
 template <class T, int D, int W, bool APPEND>
 __device__ __forceinline__ void tile_commit(const AttnArgs& a, const int32_t* bt, int hk, int j0, int jmax,
                                             const TileStage<T, D, W>& stg, unsigned char* k_lds,
-                                            unsigned char* v_lds, const Append& ap) {
+                                            unsigned char* v_lds, const Append& ap, int tid = -1) {
   using G_ = TileGeom<T, D>;
   constexpr int PER = TileStage<T, D, W>::PER;
+  const int t = tid < 0 ? static_cast<int>(threadIdx.x) : tid;
   if constexpr (APPEND) {
     // the writer stores this call's new rows (only the tiles reaching them)
     if (ap.writer && j0 + KT > ap.n_old) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int qi = threadIdx.x + i * 64 * W;
+        const int qi = t + i * 64 * W;
         const int row = qi / G_::CPR, part = qi % G_::CPR;
         const int j = j0 + row;
         const int jc = min(j, jmax - 1);
@@ -310,7 +318,7 @@ __device__ __forceinline__ void tile_commit(const AttnArgs& a, const int32_t* bt
   // piece i of this lane is tile row row0 + i * STEP, 16-byte part `part`
   constexpr int STEP = 64 * W / G_::CPR;
   static_assert(STEP * G_::CPR == 64 * W, "a work group's pieces cover whole rows");
-  const int row0 = threadIdx.x / G_::CPR, part = threadIdx.x % G_::CPR;
+  const int row0 = t / G_::CPR, part = t % G_::CPR;
   if (j0 + KT > jmax) {  // rows past jmax read as zero
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
