@@ -180,3 +180,39 @@ def test_dispatch_orders_keep_bits(dtype, shape):
     gc.assert_bitwise(res[0], full, "decode vs full path")
     if dtype == "bf16":
         gc.check_oracle(case, *res[0], seq_ids=[0, B - 1])
+
+
+@pytest.mark.parametrize("batch", [65, 100, 128])
+def test_ragged_rows_lookups(batch):
+    """Between 64 and 128 sequences the merge's and the append's row -> sequence lookups take the
+    wave-wide search; ragged row counts (0 to 3 rows per sequence, empty ones among them), bitwise
+    against the full path, the oracle on sampled sequences, and 0-3 appended rows per sequence
+    exactly where host indexing puts them."""
+    announce(f"ragged-row lookups, batch {batch}")
+    B, HK, D, BS = batch, 4, 64, 16
+    rows = [(b * 7) % 4 for b in range(B)]
+    rows[-1] = 3                                  # the last sequence has rows
+    case = gc.make_case(9900 + batch, "bf16", B, 8, HK, D, BS, 3000, "interleaved", True, rows)
+    sl = [max(int(x), 3) for x in case.seqlens]
+    sl[1] = 1025
+    case.seqlens = sl
+    out, lse = gc.run(case)
+    gc.assert_bitwise(gc.run(case, path=2), (out, lse), "full path")
+    gc.check_oracle(case, out, lse, seq_ids=[1, B // 2 + 1, B - 1])
+    g = torch.Generator().manual_seed(9901 + batch)
+    total = case.cu[-1]
+    kn = gen.randn((total, HK, D), "bf16", generator=g).to(gc.DEV)
+    vn = gen.randn((total, HK, D), "bf16", generator=g).to(gc.DEV)
+    before = torch.tensor([s - r for s, r in zip(sl, rows)], dtype=torch.int32, device=gc.DEV)
+    cu = case.cu_d()
+    pk, pv = case.pool.k.clone(), case.pool.v.clone()
+    want_k, want_v = pk.clone(), pv.clone()
+    pkv.cache_write(kn, vn, pk, pv, case.block_table, before, cu)
+    seq = torch.repeat_interleave(torch.arange(B, device=gc.DEV), torch.tensor(rows, device=gc.DEV))
+    pos = before.long()[seq] + (torch.arange(total, device=gc.DEV) - cu.long()[seq])
+    blk = case.block_table.long()[seq, pos // BS]
+    want_k[blk, pos % BS] = kn
+    want_v[blk, pos % BS] = vn
+    torch.cuda.synchronize()
+    assert torch.equal(pk.view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(pv.view(torch.int16), want_v.view(torch.int16))
