@@ -10,7 +10,9 @@
 //                             and bf16 when the grid exceeds 1024 work items.
 //   attn_kernel<SPLIT=true>   more columns (or fp32): 8 waves x 16 columns
 //                             sharing LDS tiles (bf16/FP8: three tile buffers,
-//                             the odd waves' P.V one tile late).
+//                             the odd waves' P.V one tile late; with at most 96
+//                             columns the two column-less waves load and stage
+//                             every tile and the others only compute).
 //   decode_plan_kernel        ragged batches: prefix counts for the one-wave
 //                             kernels' longest-first job order.
 // Full (prefill) path: one work item per (sequence, KV head, column block)
